@@ -1,0 +1,271 @@
+/*
+ * moe_oracle.c — fp64 CPU oracle for the W4A16 grouped-quantized MoE layer.
+ *
+ * TEST INFRASTRUCTURE ONLY (see moe_oracle.h for what it follows).  Every
+ * quantity is computed in double precision with explicit loops in the order
+ * the definition states; there is no blocking, fusion or reordering.  OpenMP,
+ * when present, only splits independent output rows across threads.
+ */
+#include "moe_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* bf16 is the upper half of an IEEE float32. */
+double oracle_bf16_to_f64(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* Round a double to the nearest bf16 (ties to even) directly, without going
+ * through float32 first.  bf16 keeps 8 significant bits; its smallest
+ * subnormal step is 2^-133 and its largest finite value (2 - 2^-7) * 2^127. */
+uint16_t oracle_f64_to_bf16(double v) {
+  if (isnan(v)) return 0x7FC0;
+  int neg = signbit(v) ? 1 : 0;
+  double a = fabs(v);
+  double r;
+  if (a == 0.0) {
+    r = 0.0;
+  } else {
+    int e;
+    frexp(a, &e);                 /* a = m * 2^e, m in [0.5, 1) */
+    int qexp = e - 8;             /* step between neighbouring bf16 values */
+    if (qexp < -133) qexp = -133; /* subnormal range: fixed step */
+    r = nearbyint(ldexp(a, -qexp)); /* default rounding mode: ties to even */
+    r = ldexp(r, qexp);
+  }
+  const double maxf = ldexp(255.0, 120); /* (2 - 2^-7) * 2^127 */
+  uint16_t bits;
+  if (r > maxf) {
+    bits = 0x7F80; /* overflow -> inf */
+  } else {
+    float f = (float)r; /* exact: r has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    bits = (uint16_t)(u >> 16);
+  }
+  return (uint16_t)(bits | (neg ? 0x8000 : 0));
+}
+
+void oracle_f64_to_bf16_array(const double* v, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_f64_to_bf16(v[i]);
+}
+
+/* The stored 4-bit code of element (n, k) of an N x K matrix whose rows hold
+ * K/2 bytes: the low nibble carries the even k, the high nibble the odd k. */
+static int code_at(const uint8_t* q, int32_t K, int32_t n, int32_t k) {
+  uint8_t byte = q[(int64_t)n * (K / 2) + k / 2];
+  return (k % 2 == 0) ? (byte & 0xF) : (byte >> 4);
+}
+
+/* Symmetric INT4 with one bf16 scale per group of G consecutive k. */
+static double wq_at(const uint8_t* q, const uint16_t* s, int32_t K, int32_t G,
+                    int32_t n, int32_t k) {
+  int code = code_at(q, K, n, k);
+  double scale = oracle_bf16_to_f64(s[(int64_t)n * (K / G) + k / G]);
+  return (double)(code - 8) * scale;
+}
+
+int oracle_dequant(const uint8_t* q, const uint16_t* s, int32_t N, int32_t K,
+                   int32_t G, double* W) {
+  if (!q || !s || !W || N < 0 || K <= 0 || G <= 0 || K % G || K % 2) return -1;
+  for (int32_t n = 0; n < N; ++n)
+    for (int32_t k = 0; k < K; ++k)
+      W[(int64_t)n * K + k] = wq_at(q, s, K, G, n, k);
+  return 0;
+}
+
+static double silu(double g) { return g / (1.0 + exp(-g)); }
+
+int oracle_route(const oracle_cfg* cfg, const float* router_w, const uint16_t* x,
+                 int32_t M, int32_t* ids, double* w, double* gap, double* logits) {
+  if (!cfg || !router_w || (!x && M > 0) || !ids || !w || M < 0) return -1;
+  const int32_t H = cfg->hidden, E = cfg->n_experts, k = cfg->top_k;
+  if (H <= 0 || E <= 0 || k < 1 || k > E) return -1;
+  double* l = (double*)malloc(sizeof(double) * (size_t)E);
+  char* taken = (char*)malloc((size_t)E);
+  if (!l || !taken) { free(l); free(taken); return -2; }
+  for (int32_t t = 0; t < M; ++t) {
+    const uint16_t* xt = x + (int64_t)t * H;
+    for (int32_t e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int32_t h = 0; h < H; ++h)
+        acc += oracle_bf16_to_f64(xt[h]) * (double)router_w[(int64_t)e * H + h];
+      l[e] = acc;
+      if (logits) logits[(int64_t)t * E + e] = acc;
+    }
+    /* Selection: k passes, each taking the largest logit not yet taken; a
+     * strict comparison keeps the lower id on ties. */
+    memset(taken, 0, (size_t)E);
+    for (int32_t j = 0; j < k; ++j) {
+      int32_t best = -1;
+      for (int32_t e = 0; e < E; ++e)
+        if (!taken[e] && (best < 0 || l[e] > l[best])) best = e;
+      taken[best] = 1;
+      ids[(int64_t)t * k + j] = best;
+    }
+    if (gap) {
+      if (k == E) {
+        gap[t] = INFINITY;
+      } else {
+        int32_t next = -1;
+        for (int32_t e = 0; e < E; ++e)
+          if (!taken[e] && (next < 0 || l[e] > l[next])) next = e;
+        gap[t] = l[ids[(int64_t)t * k + k - 1]] - l[next];
+      }
+    }
+    /* Softmax over the chosen logits, shifted by the largest for range. */
+    const double l0 = l[ids[(int64_t)t * k]];
+    double denom = 0.0;
+    for (int32_t j = 0; j < k; ++j) denom += exp(l[ids[(int64_t)t * k + j]] - l0);
+    for (int32_t j = 0; j < k; ++j)
+      w[(int64_t)t * k + j] = exp(l[ids[(int64_t)t * k + j]] - l0) / denom;
+  }
+  free(l);
+  free(taken);
+  return 0;
+}
+
+int oracle_expert_q(const oracle_cfg* cfg, const uint8_t* w13_q, const uint16_t* w13_s,
+                    const uint8_t* w2_q, const uint16_t* w2_s, const double* x,
+                    double* h_out, double* y) {
+  if (!cfg || !w13_q || !w13_s || !w2_q || !w2_s || !x || !y) return -1;
+  const int32_t H = cfg->hidden, I = cfg->inter, G = cfg->group_size;
+  double* h = (double*)malloc(sizeof(double) * (size_t)I);
+  if (!h) return -2;
+#pragma omp parallel for schedule(static)
+  for (int32_t r = 0; r < I; ++r) {
+    double g = 0.0, u = 0.0;
+    for (int32_t k = 0; k < H; ++k) {
+      g += wq_at(w13_q, w13_s, H, G, r, k) * x[k];       /* gate row r     */
+      u += wq_at(w13_q, w13_s, H, G, I + r, k) * x[k];   /* up row I + r   */
+    }
+    h[r] = silu(g) * u;
+  }
+#pragma omp parallel for schedule(static)
+  for (int32_t n = 0; n < H; ++n) {
+    double acc = 0.0;
+    for (int32_t r = 0; r < I; ++r) acc += wq_at(w2_q, w2_s, I, G, n, r) * h[r];
+    y[n] = acc;
+  }
+  if (h_out) memcpy(h_out, h, sizeof(double) * (size_t)I);
+  free(h);
+  return 0;
+}
+
+int oracle_expert_dense(const oracle_cfg* cfg, const uint16_t* sh_w13,
+                        const uint16_t* sh_w2, const double* x, double* h_out,
+                        double* y) {
+  if (!cfg || !sh_w13 || !sh_w2 || !x || !y) return -1;
+  const int32_t H = cfg->hidden, I = cfg->inter;
+  double* h = (double*)malloc(sizeof(double) * (size_t)I);
+  if (!h) return -2;
+#pragma omp parallel for schedule(static)
+  for (int32_t r = 0; r < I; ++r) {
+    double g = 0.0, u = 0.0;
+    for (int32_t k = 0; k < H; ++k) {
+      g += oracle_bf16_to_f64(sh_w13[(int64_t)r * H + k]) * x[k];
+      u += oracle_bf16_to_f64(sh_w13[(int64_t)(I + r) * H + k]) * x[k];
+    }
+    h[r] = silu(g) * u;
+  }
+#pragma omp parallel for schedule(static)
+  for (int32_t n = 0; n < H; ++n) {
+    double acc = 0.0;
+    for (int32_t r = 0; r < I; ++r) acc += oracle_bf16_to_f64(sh_w2[(int64_t)n * I + r]) * h[r];
+    y[n] = acc;
+  }
+  if (h_out) memcpy(h_out, h, sizeof(double) * (size_t)I);
+  free(h);
+  return 0;
+}
+
+int oracle_forward(const oracle_cfg* cfg, const oracle_experts* ex,
+                   const uint16_t* x, int32_t M, const int32_t* ids,
+                   const double* w, double* out) {
+  if (!cfg || !ex || M < 0 || (M > 0 && (!x || !ids || !w || !out))) return -1;
+  const int32_t H = cfg->hidden, E = cfg->n_experts, k = cfg->top_k;
+  if (cfg->has_shared && (!ex->sh_w13 || !ex->sh_w2)) return -1;
+  double* xt = (double*)malloc(sizeof(double) * (size_t)H);
+  double* y = (double*)malloc(sizeof(double) * (size_t)H);
+  if (!xt || !y) { free(xt); free(y); return -2; }
+  int bad = 0;
+  for (int32_t t = 0; t < M; ++t) {
+    for (int32_t h = 0; h < H; ++h) xt[h] = oracle_bf16_to_f64(x[(int64_t)t * H + h]);
+    double* ot = out + (int64_t)t * H;
+    for (int32_t n = 0; n < H; ++n) ot[n] = 0.0;
+    for (int32_t j = 0; j < k; ++j) {
+      const int32_t e = ids[(int64_t)t * k + j];
+      if (e < 0 || e >= E) { ++bad; continue; }
+      if (!ex->w13_q[e] || !ex->w13_s[e] || !ex->w2_q[e] || !ex->w2_s[e]) {
+        free(xt); free(y);
+        return -3; /* selected expert not supplied */
+      }
+      oracle_expert_q(cfg, ex->w13_q[e], ex->w13_s[e], ex->w2_q[e], ex->w2_s[e], xt, NULL, y);
+      const double wj = w[(int64_t)t * k + j];
+      for (int32_t n = 0; n < H; ++n) ot[n] += wj * y[n];
+    }
+    if (cfg->has_shared) {
+      oracle_expert_dense(cfg, ex->sh_w13, ex->sh_w2, xt, NULL, y);
+      for (int32_t n = 0; n < H; ++n) ot[n] += y[n];
+    }
+  }
+  free(xt);
+  free(y);
+  return bad;
+}
+
+int oracle_permute(const int32_t* ids, int32_t M, int32_t k, int32_t E,
+                   int32_t* counts, int32_t* offsets, int32_t* perm) {
+  if (M < 0 || k < 1 || E < 1 || !counts || !offsets || (M > 0 && (!ids || !perm))) return -1;
+  int bad = 0;
+  for (int32_t e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t p = 0; p < (int64_t)M * k; ++p) {
+    int32_t e = ids[p];
+    if (e < 0 || e >= E) { ++bad; continue; }
+    counts[e] += 1;
+  }
+  offsets[0] = 0;
+  for (int32_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  /* Fill by scanning pairs in ascending order: stable inside each expert. */
+  int32_t* cursor = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+  if (!cursor) return -2;
+  for (int32_t e = 0; e < E; ++e) cursor[e] = offsets[e];
+  for (int64_t p = 0; p < (int64_t)M * k; ++p) {
+    int32_t e = ids[p];
+    if (e < 0 || e >= E) continue;
+    perm[cursor[e]++] = (int32_t)p;
+  }
+  free(cursor);
+  return bad;
+}
+
+int oracle_rmsnorm(const uint16_t* y, int32_t M, int32_t H, double eps, uint16_t* out) {
+  if (M < 0 || H <= 0 || (M > 0 && (!y || !out))) return -1;
+  for (int32_t t = 0; t < M; ++t) {
+    double ss = 0.0;
+    for (int32_t h = 0; h < H; ++h) {
+      double v = oracle_bf16_to_f64(y[(int64_t)t * H + h]);
+      ss += v * v;
+    }
+    const double d = sqrt(ss / (double)H + eps);
+    for (int32_t h = 0; h < H; ++h)
+      out[(int64_t)t * H + h] = oracle_f64_to_bf16(oracle_bf16_to_f64(y[(int64_t)t * H + h]) / d);
+  }
+  return 0;
+}
