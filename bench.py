@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 grouped-quantized MoE layer on one MI355X.
+
+Default workload (one "step" = one decode token through one Ling-shape MoE
+layer: route + gate_up/SiLU + down + weighted combine + shared expert, M = 1):
+  hidden 2560, 512 routed experts, top-8, moe_intermediate 768, INT4 g32
+  routed experts with bf16 scales, bf16 shared expert, fp32 router.
+Steps rotate over C resident copies of the layer (distinct device memory,
+distinct seeded routers), so a step never finds its weights in the 256 MB
+last-level cache; the step chain is captured once in a HIP graph and
+replayed.  Throughput is algorithmic bytes per step / time (GB/s) and
+microseconds per token.
+
+Other workloads (for measurement runs; the default is the one reported):
+  --workload verify2 / verify4   M = 2 / 4 tokens per step (speculative verify)
+  --workload stack               one token through 40 stacked layers with
+                                 RMSNorm between them (one step = 40 layers)
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+# Algorithmic bytes (Ling shape): every weight byte a step must read once,
+# plus activations in and out.
+EXPERT_GU_BYTES = 2 * 768 * 2560 // 2 + 2 * 768 * (2560 // 32) * 2     # 2,211,840
+EXPERT_DN_BYTES = 2560 * 768 // 2 + 2560 * (768 // 32) * 2             # 1,105,920
+EXPERT_BYTES = EXPERT_GU_BYTES + EXPERT_DN_BYTES                        # 3,317,760
+SHARED_GU_BYTES = 2 * 768 * 2560 * 2                                    # 7,864,320
+SHARED_DN_BYTES = 2560 * 768 * 2                                        # 3,932,160
+ROUTER_BYTES = 512 * 2560 * 4                                           # 5,242,880
+TOKEN_IO_BYTES = 2 * 2560 * 2                                           # x in, out back
+
+
+def step_bytes(n_unique_experts: int, M: int) -> int:
+    return n_unique_experts * EXPERT_BYTES + SHARED_GU_BYTES + SHARED_DN_BYTES + ROUTER_BYTES + M * TOKEN_IO_BYTES
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=4096)
+    p.add_argument("--warmup", type=int, default=512)
+    p.add_argument("--workload", default="decode", choices=["decode", "verify2", "verify4", "stack"])
+    p.add_argument("--copies", type=int, default=32, help="resident layer copies to rotate over")
+    p.add_argument("--chunk", type=int, default=256, help="steps captured per graph")
+    p.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--stage-steps", type=int, default=256, help="eager steps timed per stage")
+    return p.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the layer's sharding is described in DESIGN.md); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from w4a16_grouped_quantized_amd import binding as B
+    from w4a16_grouped_quantized_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    B.lib()
+    shape = synth.LING
+    cfg = B.config(shape)
+    M = {"decode": 1, "verify2": 2, "verify4": 4, "stack": 1}[args.workload]
+    n_layers = 40 if args.workload == "stack" else args.copies
+
+    t0 = time.time()
+    layer = synth.make_layer(shape, 1, threads=16)
+    base = B.MoeLayer(layer)
+    log(f"layer generated and packed in {time.time() - t0:.1f}s; build: {B.build_info()}")
+
+    # C copies: distinct device memory; distinct seeded routers (layer seeds 1000 + c).
+    copies = []
+    for c in range(n_layers):
+        packed = base.packed if c == 0 else base.packed.clone()
+        router = torch.from_numpy(synth.make_router(shape, 1000 + c)).cuda()
+        copies.append((packed, router))
+    torch.cuda.synchronize()
+    log(f"{n_layers} resident copies ({n_layers * (base.packed.numel() + 5242880) / 1e9:.1f} GB)")
+
+    ws = B.Workspace(cfg, max(M, 1))
+    stream = torch.cuda.current_stream()
+    chunk = max(1, min(args.chunk, args.steps))
+    n_tok = chunk * M
+    X = torch.from_numpy(synth.make_tokens(shape, 2, n_tok).view(np.int16)).view(torch.bfloat16).cuda()
+    ids = torch.empty((chunk, M, shape.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((chunk, M, shape.top_k), dtype=torch.float32, device="cuda")
+    out = torch.empty((chunk, M, shape.hidden), dtype=torch.bfloat16, device="cuda")
+    xn = torch.empty((chunk, M, shape.hidden), dtype=torch.bfloat16, device="cuda")
+
+    def run_steps(lo, hi, step_offset):
+        """Enqueue steps lo..hi-1 (the graph body)."""
+        for i in range(lo, hi):
+            s = step_offset + i
+            if args.workload == "stack":
+                # one token through all layers; layer l reads the previous output
+                x_in = X[i * M:(i + 1) * M]
+                for l in range(n_layers):
+                    pk, rt = copies[l]
+                    if l == 0:
+                        B.route(cfg, rt, x_in, ids[i], w[i], ws.buf)
+                        B.forward(cfg, pk, x_in, ids[i], w[i], out[i], ws.buf)
+                    else:
+                        B.route(cfg, rt, out[i], ids[i], w[i], ws.buf, flags=B.MOE_F_INPUT_RMSNORM, x_norm=xn[i])
+                        B.forward(cfg, pk, xn[i], ids[i], w[i], out[i], ws.buf)
+            else:
+                pk, rt = copies[s % n_layers]
+                x_in = X[i * M:(i + 1) * M]
+                B.route(cfg, rt, x_in, ids[i], w[i], ws.buf)
+                B.forward(cfg, pk, x_in, ids[i], w[i], out[i], ws.buf)
+
+    # warm the stream outside capture, then capture one chunk
+    run_steps(0, chunk, 0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run_steps(0, chunk, 0)
+    reps = max(1, args.steps // chunk)
+    steps = reps * chunk
+    wreps = max(1, args.warmup // chunk)
+    for _ in range(wreps):
+        g.replay()
+    torch.cuda.synchronize()
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    tw = time.perf_counter()
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - tw
+    ms = e0.elapsed_time(e1)
+    ms_per_step = ms / steps
+
+    ids_np = ids.cpu().numpy()
+    if args.workload == "stack":
+        uniq = 8.0  # per layer at M = 1
+        bytes_per_step = n_layers * step_bytes(8, 1)
+    else:
+        uniq = float(np.mean([len(np.unique(ids_np[i])) for i in range(chunk)]))
+        bytes_per_step = float(np.mean([step_bytes(len(np.unique(ids_np[i])), M) for i in range(chunk)]))
+    gbs = bytes_per_step / (ms_per_step * 1e-3) / 1e9
+    log(f"{steps} steps in {ms:.2f} ms (wall {wall * 1e3:.2f} ms): {ms_per_step * 1e3:.2f} us/step, "
+        f"{gbs:.0f} GB/s, unique experts/step {uniq:.2f}")
+
+    # Per-stage kernel durations, eager, HIP events on the launch stream around
+    # each single-kernel call (route, gate_up, down) for the same rotation.
+    def time_stages(n):
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n)]
+        for i in range(n):
+            pk, rt = copies[i % n_layers]
+            j = i % chunk
+            x_in = X[j * M:(j + 1) * M]
+            e = ev[i]
+            e[0].record(stream)
+            B.route(cfg, rt, x_in, ids[j], w[j], ws.buf)
+            e[1].record(stream)
+            e[2].record(stream)
+            B.gate_up(cfg, pk, x_in, ids[j], ws.buf)
+            e[3].record(stream)
+            e[4].record(stream)
+            B.down(cfg, pk, ids[j], w[j], out[j], ws.buf)
+            e[5].record(stream)
+        torch.cuda.synchronize()
+        r = np.array([[e[2 * s].elapsed_time(e[2 * s + 1]) for s in range(3)] for e in ev]) * 1e3
+        return np.median(r, axis=0), np.mean(r, axis=0)
+
+    time_stages(min(32, args.stage_steps))
+    st_med, st_mean = time_stages(args.stage_steps)
+    log(f"stage us (median) route {st_med[0]:.2f} gate_up {st_med[1]:.2f} down {st_med[2]:.2f}; "
+        f"(mean) {st_mean[0]:.2f} {st_mean[1]:.2f} {st_mean[2]:.2f}")
+    gu_bytes = (uniq if args.workload != "stack" else 8) * EXPERT_GU_BYTES + SHARED_GU_BYTES + M * 2560 * 2
+    achieved = gu_bytes / (st_mean[1] * 1e-6) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(shape, layer, args.cpu_baseline_seconds)
+
+    dtype = "bf16 activations, int4 weights, fp32 accumulate"
+    line = {
+        "metric": "MoE layer us/token and achieved HBM GB/s at batch 1 (W4A16 g32, top-8 of 512)",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        # per token per layer
+        "us_per_token": round(ms_per_step * 1e3 / (M if args.workload != "stack" else n_layers), 3),
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": wreps * chunk,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": {"decode": "ling_moe_layer_decode_m1", "verify2": "ling_moe_layer_verify_m2",
+                         "verify4": "ling_moe_layer_verify_m4", "stack": "ling_moe_stack40_decode_m1"}[args.workload],
+            "hidden": 2560, "n_experts": 512, "top_k": 8, "moe_intermediate": 768, "group_size": 32,
+            "tokens_per_step": M, "resident_layer_copies": n_layers, "graph_steps_per_replay": chunk,
+            "algorithmic_bytes_per_step": int(bytes_per_step), "unique_experts_per_step": uniq,
+            "compute": dtype,
+        },
+        "stage_us": {"route": round(float(st_mean[0]), 3), "gate_up": round(float(st_mean[1]), 3),
+                     "down_combine": round(float(st_mean[2]), 3)},
+        "roofline": {"bound": "hbm", "kernel": "k_gate_up (routed int4 gate_up + SiLU, shared bf16 gate_up)",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(gu_bytes)},
+        "cpu_baseline": cpu,
+        "build": B.build_info(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(shape, layer, seconds):
+    """The oracle (fp64, plain loops) on host cores: route + forward for as
+    many decode tokens of the same layer as fit in about `seconds`."""
+    from oracle import oracle as O
+    O.lib()
+    threads = O.num_threads()
+    from w4a16_grouped_quantized_amd import synth
+    x = synth.make_tokens(shape, 2, 4096)
+    # warm-up token
+    ids, w, _, _ = O.route(shape, layer.router_w, x[:1])
+    O.forward(shape, layer, x[:1], ids, w)
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds and n < x.shape[0] - 1:
+        xt = x[1 + n:2 + n]
+        ids, w, _, _ = O.route(shape, layer.router_w, xt)
+        O.forward(shape, layer, xt, ids, w)
+        n += 1
+    dt = time.perf_counter() - t0
+    us = dt / n * 1e6
+    gbs = step_bytes(8, 1) / (us * 1e-6) / 1e9
+    log(f"cpu baseline (oracle): {n} tokens in {dt:.1f}s, {us:.0f} us/token, {threads} threads")
+    return {"value": round(gbs, 4), "unit": "GB/s", "us_per_token": round(us, 1), "cores": threads,
+            "kind": "oracle", "sample": f"{n} decode tokens (M=1) of the seed-1 Ling-shape layer, route + forward"}
+
+
+if __name__ == "__main__":
+    main()

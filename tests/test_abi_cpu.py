@@ -1,0 +1,114 @@
+"""The C-ABI library loads, exports every symbol include/moe_w4a16.h declares,
+and rejects bad arguments before launching anything (no GPU needed: every case
+here fails validation, so no HIP call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from w4a16_grouped_quantized_amd import binding as B
+from w4a16_grouped_quantized_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_w4a16.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libmoe_w4a16.so is not built (python -m w4a16_grouped_quantized_amd.build)")
+    return B.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = header_functions()
+    assert set(declared) == set(B.EXPORTS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_build_info_and_status_strings(lib):
+    info = B.build_info()
+    assert "gfx950" in info and "layout=" in info
+    for rc in range(0, -8, -1):
+        assert B.status_string(rc) and B.status_string(rc) != "unknown status"
+    assert B.status_string(-99) == "unknown status"
+
+
+def _cfg(**kw):
+    d = dict(hidden=2560, n_experts=512, top_k=8, inter=768, group_size=32, has_shared=1)
+    d.update(kw)
+    return B.MoeConfig(**d)
+
+
+def test_sizes(lib):
+    c = B.config(synth.LING)
+    # packed blob = plain bytes (routed codes + scales + shared), each section 256-aligned
+    E, H, I = 512, 2560, 768
+    plain = E * (2 * I * H // 2 + 2 * I * (H // 32) * 2 + H * I // 2 + H * (I // 32) * 2) + (2 * I * H + H * I) * 2
+    assert B.packed_size(c) == plain
+    assert B.workspace_size(c, 1) > 0
+    assert B.workspace_size(c, 4) > B.workspace_size(c, 1)
+    assert B.packed_size(_cfg(group_size=64)) == 0
+    assert B.workspace_size(_cfg(hidden=100), 1) == 0
+    assert B.workspace_size(c, -1) == 0
+
+
+@pytest.mark.parametrize("kw,rc", [
+    (dict(group_size=64), -5),
+    (dict(hidden=100), -2),
+    (dict(hidden=0), -2),
+    (dict(inter=40), -2),
+    (dict(top_k=0), -2),
+    (dict(top_k=600, n_experts=512), -2),
+    (dict(n_experts=1024, top_k=8), -5),
+    (dict(top_k=65, n_experts=128), -5),
+    (dict(has_shared=2), -2),
+    (dict(hidden=8192), -5),
+])
+def test_config_validation(lib, kw, rc):
+    c = _cfg(**kw)
+    fake = ctypes.c_void_p(0x10000)
+    got = lib.moe_route(ctypes.byref(c), fake, fake, 1, 0, None, fake, fake, fake, 1 << 30, None)
+    assert got == rc
+    got = lib.moe_forward_w4a16(ctypes.byref(c), fake, fake, 1, fake, fake, fake, fake, 1 << 30, None)
+    assert got == rc
+
+
+def test_pointer_and_size_validation(lib):
+    c = _cfg()
+    a = ctypes.c_void_p(0x10000)     # aligned, never dereferenced: every call below fails a check
+    odd = ctypes.c_void_p(0x10001)
+    big = 1 << 40
+    assert lib.moe_route(None, a, a, 1, 0, None, a, a, a, big, None) == -1
+    assert lib.moe_route(ctypes.byref(c), None, a, 1, 0, None, a, a, a, big, None) == -1
+    assert lib.moe_route(ctypes.byref(c), a, a, 1, B.MOE_F_INPUT_RMSNORM, None, a, a, a, big, None) == -1
+    assert lib.moe_route(ctypes.byref(c), a, a, 1, 0x8, None, a, a, a, big, None) == -2
+    assert lib.moe_route(ctypes.byref(c), a, a, -1, 0, None, a, a, a, big, None) == -2
+    assert lib.moe_route(ctypes.byref(c), a, odd, 1, 0, None, a, a, a, big, None) == -3
+    assert lib.moe_route(ctypes.byref(c), a, a, 1, 0, None, a, a, a, 16, None) == -4
+    # M = 0 is a no-op and succeeds without touching any pointer
+    assert lib.moe_route(ctypes.byref(c), None, None, 0, 0, None, None, None, None, 0, None) == 0
+    assert lib.moe_forward_w4a16(ctypes.byref(c), None, None, 0, None, None, None, None, 0, None) == 0
+    assert lib.moe_forward_w4a16(ctypes.byref(c), a, a, 1, a, a, None, a, big, None) == -1
+    assert lib.moe_forward_w4a16(ctypes.byref(c), odd, a, 1, a, a, a, a, big, None) == -3
+    assert lib.moe_forward_w4a16(ctypes.byref(c), a, a, 1, a, a, a, a, 64, None) == -4
+    # more slots than the decode kernels take
+    assert lib.moe_forward_w4a16(ctypes.byref(c), a, a, 1 << 12, a, a, a, a, big, None) == -5
+    assert lib.moe_permute(ctypes.byref(c), a, 4, None, a, a, a, big, None) == -1
+    assert lib.moe_permute(ctypes.byref(c), a, 4, a, a, a, a, 8, None) == -4
+    w = B.MoeWeightsPlain(a, a, a, a, None, None)   # shared expert missing while has_shared = 1
+    assert lib.moe_pack_weights(ctypes.byref(c), ctypes.byref(w), a, big, None) == -1
+    w = B.MoeWeightsPlain(a, a, a, a, a, a)
+    assert lib.moe_pack_weights(ctypes.byref(c), ctypes.byref(w), a, 1024, None) == -4
+    assert lib.moe_workspace_init(None, 64, None) == -1
+    assert lib.moe_workspace_init(odd, 64, None) == -3
+    code = ctypes.c_int32(0)
+    assert lib.moe_get_device_error(None, None, ctypes.byref(code)) == -1

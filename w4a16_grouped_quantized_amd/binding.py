@@ -1,0 +1,209 @@
+"""ctypes binding of libmoe_w4a16.so (include/moe_w4a16.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  torch supplies device memory and the current stream.  The library
+must be built (``python -m w4a16_grouped_quantized_amd.build``); a missing
+library is an error, never a fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_w4a16.so")
+
+MOE_F_INPUT_RMSNORM = 0x1
+
+MOE_OK = 0
+STATUS_NAMES = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_ALIGN",
+                -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_UNSUPPORTED", -6: "MOE_ERR_LAUNCH",
+                -7: "MOE_ERR_DEVICE"}
+
+# Every symbol include/moe_w4a16.h declares.
+EXPORTS = ("moe_packed_size", "moe_pack_weights", "moe_workspace_size", "moe_workspace_init",
+           "moe_route", "moe_forward_w4a16", "moe_gate_up_w4a16", "moe_down_w4a16", "moe_permute",
+           "moe_get_device_error", "moe_status_string", "moe_build_info")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: {STATUS_NAMES.get(status, status)} ({msg})")
+        self.status = status
+
+
+class MoeConfig(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("group_size", ctypes.c_int32), ("has_shared", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+
+
+class MoeWeightsPlain(ctypes.Structure):
+    _fields_ = [("w13_q", _P), ("w13_s", _P), ("w2_q", _P), ("w2_s", _P),
+                ("sh_w13", _P), ("sh_w2", _P)]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is not built; run python -m w4a16_grouped_quantized_amd.build")
+            L = ctypes.CDLL(LIB_PATH)
+            cfgp = ctypes.POINTER(MoeConfig)
+            L.moe_packed_size.restype = ctypes.c_size_t
+            L.moe_packed_size.argtypes = [cfgp]
+            L.moe_pack_weights.argtypes = [cfgp, ctypes.POINTER(MoeWeightsPlain), _P, ctypes.c_size_t, _P]
+            L.moe_workspace_size.restype = ctypes.c_size_t
+            L.moe_workspace_size.argtypes = [cfgp, ctypes.c_int32]
+            L.moe_workspace_init.argtypes = [_P, ctypes.c_size_t, _P]
+            L.moe_route.argtypes = [cfgp, _P, _P, ctypes.c_int32, ctypes.c_uint32, _P, _P, _P, _P,
+                                    ctypes.c_size_t, _P]
+            L.moe_forward_w4a16.argtypes = [cfgp, _P, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t, _P]
+            L.moe_gate_up_w4a16.argtypes = [cfgp, _P, _P, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]
+            L.moe_down_w4a16.argtypes = [cfgp, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t, _P]
+            L.moe_permute.argtypes = [cfgp, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t, _P]
+            L.moe_get_device_error.argtypes = [_P, _P, ctypes.POINTER(ctypes.c_int32)]
+            L.moe_status_string.restype = ctypes.c_char_p
+            L.moe_status_string.argtypes = [ctypes.c_int]
+            L.moe_build_info.restype = ctypes.c_char_p
+            L.moe_build_info.argtypes = []
+            _lib = L
+        return _lib
+
+
+def config(shape) -> MoeConfig:
+    return MoeConfig(shape.hidden, shape.n_experts, shape.top_k, shape.inter, shape.group_size,
+                     int(shape.has_shared))
+
+
+def _check(fn: str, rc: int):
+    if rc != MOE_OK:
+        raise MoeError(fn, rc, lib().moe_status_string(rc).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def build_info() -> str:
+    return lib().moe_build_info().decode()
+
+
+def status_string(rc: int) -> str:
+    return lib().moe_status_string(rc).decode()
+
+
+def packed_size(cfg: MoeConfig) -> int:
+    return lib().moe_packed_size(ctypes.byref(cfg))
+
+
+def workspace_size(cfg: MoeConfig, max_tokens: int) -> int:
+    return lib().moe_workspace_size(ctypes.byref(cfg), max_tokens)
+
+
+def pack_weights(cfg, w13_q, w13_s, w2_q, w2_s, sh_w13, sh_w2, packed, stream=None):
+    src = MoeWeightsPlain(_ptr(w13_q), _ptr(w13_s), _ptr(w2_q), _ptr(w2_s), _ptr(sh_w13), _ptr(sh_w2))
+    _check("moe_pack_weights", lib().moe_pack_weights(ctypes.byref(cfg), ctypes.byref(src), _ptr(packed),
+                                                      packed.numel() * packed.element_size(), _stream(stream)))
+
+
+def workspace_init(ws, stream=None):
+    _check("moe_workspace_init", lib().moe_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def route(cfg, router_w, x, topk_ids, topk_w, ws, flags: int = 0, x_norm=None, stream=None):
+    M = x.shape[0]
+    _check("moe_route", lib().moe_route(ctypes.byref(cfg), _ptr(router_w), _ptr(x), M, flags, _ptr(x_norm),
+                                        _ptr(topk_ids), _ptr(topk_w), _ptr(ws), ws.numel() * ws.element_size(),
+                                        _stream(stream)))
+
+
+def forward(cfg, packed, x, topk_ids, topk_w, out, ws, stream=None):
+    M = x.shape[0]
+    _check("moe_forward_w4a16", lib().moe_forward_w4a16(ctypes.byref(cfg), _ptr(packed), _ptr(x), M,
+                                                        _ptr(topk_ids), _ptr(topk_w), _ptr(out), _ptr(ws),
+                                                        ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def gate_up(cfg, packed, x, topk_ids, ws, stream=None):
+    M = x.shape[0]
+    _check("moe_gate_up_w4a16", lib().moe_gate_up_w4a16(ctypes.byref(cfg), _ptr(packed), _ptr(x), M,
+                                                        _ptr(topk_ids), _ptr(ws), ws.numel() * ws.element_size(),
+                                                        _stream(stream)))
+
+
+def down(cfg, packed, topk_ids, topk_w, out, ws, stream=None):
+    M = topk_ids.shape[0]
+    _check("moe_down_w4a16", lib().moe_down_w4a16(ctypes.byref(cfg), _ptr(packed), M, _ptr(topk_ids),
+                                                  _ptr(topk_w), _ptr(out), _ptr(ws),
+                                                  ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def permute(cfg, topk_ids, counts, offsets, perm, ws, stream=None):
+    M = topk_ids.shape[0]
+    _check("moe_permute", lib().moe_permute(ctypes.byref(cfg), _ptr(topk_ids), M, _ptr(counts), _ptr(offsets),
+                                            _ptr(perm), _ptr(ws), ws.numel() * ws.element_size(),
+                                            _stream(stream)))
+
+
+def get_device_error(ws, stream=None) -> int:
+    code = ctypes.c_int32(0)
+    rc = lib().moe_get_device_error(_ptr(ws), _stream(stream), ctypes.byref(code))
+    if rc not in (MOE_OK, -7):
+        _check("moe_get_device_error", rc)
+    return code.value
+
+
+class MoeLayer:
+    """One layer resident on the GPU: router (fp32, plain layout) and the
+    packed expert blob, built from a synth.Layer (numpy, plain layout)."""
+
+    def __init__(self, layer, device="cuda"):
+        import torch
+        self.shape = layer.shape
+        self.cfg = config(layer.shape)
+        dev = torch.device(device)
+
+        def up(a, dtype):
+            return torch.from_numpy(np.ascontiguousarray(a).view(dtype)).to(dev)
+
+        self.router_w = up(layer.router_w, np.float32)
+        n = packed_size(self.cfg)
+        if n == 0:
+            raise MoeError("moe_packed_size", -2, "invalid config")
+        self.packed = torch.empty(n, dtype=torch.uint8, device=dev)
+        w13_q, w13_s = up(layer.w13_q, np.uint8), up(layer.w13_s, np.int16)
+        w2_q, w2_s = up(layer.w2_q, np.uint8), up(layer.w2_s, np.int16)
+        sh13 = up(layer.sh_w13, np.int16) if layer.shape.has_shared else None
+        sh2 = up(layer.sh_w2, np.int16) if layer.shape.has_shared else None
+        pack_weights(self.cfg, w13_q, w13_s, w2_q, w2_s, sh13, sh2, self.packed)
+        torch.cuda.current_stream().synchronize()
+        del w13_q, w13_s, w2_q, w2_s, sh13, sh2
+
+
+class Workspace:
+    def __init__(self, cfg: MoeConfig, max_tokens: int, device="cuda"):
+        import torch
+        n = workspace_size(cfg, max_tokens)
+        if n == 0:
+            raise MoeError("moe_workspace_size", -2, "invalid config or max_tokens")
+        self.buf = torch.empty(n, dtype=torch.uint8, device=device)
+        workspace_init(self.buf)

@@ -1,0 +1,208 @@
+// api.cpp — the C ABI (include/moe_w4a16.h): argument checks, workspace and
+// packed-layout bookkeeping, and the launches.  Nothing here allocates device
+// memory or synchronises except moe_get_device_error.
+#include "moe_w4a16.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.hpp"
+
+using namespace moe;
+
+namespace {
+
+constexpr float kRmsEps = 1e-6f;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Shape checks shared by every entry point.
+int check_cfg(const moe_config* c, Shape* s) {
+  if (!c) return MOE_ERR_NULL;
+  if (c->group_size != kGroup) return MOE_ERR_UNSUPPORTED;
+  if (c->hidden <= 0 || c->hidden % 256) return MOE_ERR_SHAPE;
+  if (c->inter <= 0 || c->inter % 32) return MOE_ERR_SHAPE;
+  if (c->n_experts < 1 || c->top_k < 1 || c->top_k > c->n_experts) return MOE_ERR_SHAPE;
+  if (c->has_shared != 0 && c->has_shared != 1) return MOE_ERR_SHAPE;
+  if (c->n_experts > kMaxExperts || c->top_k > kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  if (c->hidden / kGroup > kMaxGroups || c->inter / kGroup > kMaxGroups) return MOE_ERR_UNSUPPORTED;
+  s->H = c->hidden; s->E = c->n_experts; s->k = c->top_k; s->I = c->inter; s->has_shared = c->has_shared;
+  return MOE_OK;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_packed_size(const moe_config* cfg) {
+  Shape s;
+  if (check_cfg(cfg, &s) != MOE_OK) return 0;
+  return packed_layout(s.H, s.E, s.I, s.has_shared).total;
+}
+
+int moe_pack_weights(const moe_config* cfg, const moe_weights_plain* src, void* packed, size_t packed_bytes,
+                     void* stream) {
+  Shape s;
+  int rc = check_cfg(cfg, &s);
+  if (rc != MOE_OK) return rc;
+  if (!src || !packed || !src->w13_q || !src->w13_s || !src->w2_q || !src->w2_s) return MOE_ERR_NULL;
+  if (s.has_shared ? (!src->sh_w13 || !src->sh_w2) : (src->sh_w13 || src->sh_w2)) return MOE_ERR_NULL;
+  if (!aligned16(packed) || !aligned16(src->w13_q) || !aligned16(src->w2_q) || !aligned4(src->w13_s) ||
+      !aligned4(src->w2_s) || (s.has_shared && (!aligned16(src->sh_w13) || !aligned16(src->sh_w2))))
+    return MOE_ERR_ALIGN;
+  const PackedLayout P = packed_layout(s.H, s.E, s.I, s.has_shared);
+  if (packed_bytes < P.total) return MOE_ERR_WORKSPACE;
+  return launched(launch_pack(s, src->w13_q, src->w13_s, src->w2_q, src->w2_s, src->sh_w13, src->sh_w2,
+                              static_cast<uint8_t*>(packed), P, static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_workspace_size(const moe_config* cfg, int32_t max_tokens) {
+  Shape s;
+  if (check_cfg(cfg, &s) != MOE_OK || max_tokens < 0) return 0;
+  return ws_layout(s.H, s.E, s.k, s.I, s.has_shared, max_tokens < 1 ? 1 : max_tokens).total;
+}
+
+int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws) return MOE_ERR_NULL;
+  if (!aligned16(ws)) return MOE_ERR_ALIGN;
+  return launched(launch_fill_zero(ws, ws_bytes, static_cast<hipStream_t>(stream)));
+}
+
+int moe_route(const moe_config* cfg, const float* router_w, const uint16_t* x, int32_t M, uint32_t flags,
+              uint16_t* x_norm, int32_t* topk_ids, float* topk_w, void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  int rc = check_cfg(cfg, &s);
+  if (rc != MOE_OK) return rc;
+  if (M < 0 || (flags & ~MOE_F_INPUT_RMSNORM)) return MOE_ERR_SHAPE;
+  if (M == 0) return MOE_OK;
+  const bool rms = (flags & MOE_F_INPUT_RMSNORM) != 0;
+  if (!router_w || !x || !topk_ids || !topk_w || !ws || (rms && !x_norm)) return MOE_ERR_NULL;
+  if (!aligned16(router_w) || !aligned16(x) || !aligned16(ws) || !aligned4(topk_ids) || !aligned4(topk_w) ||
+      (rms && !aligned16(x_norm)))
+    return MOE_ERR_ALIGN;
+  if (!route_supported(s)) return MOE_ERR_UNSUPPORTED;
+  const WsLayout L = ws_layout(s.H, s.E, s.k, s.I, s.has_shared, M);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  return launched(launch_route(s, router_w, x, M, rms, kRmsEps, x_norm, topk_ids, topk_w,
+                               static_cast<uint8_t*>(ws), L, static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+// Checks shared by the expert stages; x / topk_w / out are checked only when
+// the stage uses them (need_* flags).
+int check_experts(const moe_config* cfg, Shape* s, const void* packed, const uint16_t* x, int32_t M,
+                  const int32_t* topk_ids, const float* topk_w, const uint16_t* out, const void* ws,
+                  size_t ws_bytes, bool need_x, bool need_out, WsLayout* L) {
+  int rc = check_cfg(cfg, s);
+  if (rc != MOE_OK) return rc;
+  if (M < 0) return MOE_ERR_SHAPE;
+  if (M == 0) return MOE_OK;
+  if (!packed || !topk_ids || !ws || (need_x && !x) || (need_out && (!topk_w || !out))) return MOE_ERR_NULL;
+  if (!aligned16(packed) || !aligned16(ws) || !aligned4(topk_ids) || (need_x && !aligned16(x)) ||
+      (need_out && (!aligned16(out) || !aligned4(topk_w))))
+    return MOE_ERR_ALIGN;
+  if (!experts_supported(*s)) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)M * s->k > kMaxSlots) return MOE_ERR_UNSUPPORTED;
+  *L = ws_layout(s->H, s->E, s->k, s->I, s->has_shared, M);
+  if (ws_bytes < L->total) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+}  // namespace
+
+int moe_gate_up_w4a16(const moe_config* cfg, const void* packed, const uint16_t* x, int32_t M,
+                      const int32_t* topk_ids, void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  WsLayout L;
+  int rc = check_experts(cfg, &s, packed, x, M, topk_ids, nullptr, nullptr, ws, ws_bytes, true, false, &L);
+  if (rc != MOE_OK || M == 0) return rc;
+  const PackedLayout P = packed_layout(s.H, s.E, s.I, s.has_shared);
+  return launched(launch_gate_up(s, static_cast<const uint8_t*>(packed), P, x, M, topk_ids,
+                                 static_cast<uint8_t*>(ws), L, static_cast<hipStream_t>(stream)));
+}
+
+int moe_down_w4a16(const moe_config* cfg, const void* packed, int32_t M, const int32_t* topk_ids,
+                   const float* topk_w, uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  WsLayout L;
+  int rc = check_experts(cfg, &s, packed, nullptr, M, topk_ids, topk_w, out, ws, ws_bytes, false, true, &L);
+  if (rc != MOE_OK || M == 0) return rc;
+  const PackedLayout P = packed_layout(s.H, s.E, s.I, s.has_shared);
+  return launched(launch_down(s, static_cast<const uint8_t*>(packed), P, M, topk_ids, topk_w, out,
+                              static_cast<uint8_t*>(ws), L, static_cast<hipStream_t>(stream)));
+}
+
+int moe_forward_w4a16(const moe_config* cfg, const void* packed, const uint16_t* x, int32_t M,
+                      const int32_t* topk_ids, const float* topk_w, uint16_t* out, void* ws, size_t ws_bytes,
+                      void* stream) {
+  Shape s;
+  WsLayout L;
+  int rc = check_experts(cfg, &s, packed, x, M, topk_ids, topk_w, out, ws, ws_bytes, true, true, &L);
+  if (rc != MOE_OK || M == 0) return rc;
+  const PackedLayout P = packed_layout(s.H, s.E, s.I, s.has_shared);
+  const uint8_t* pk = static_cast<const uint8_t*>(packed);
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  rc = launched(launch_gate_up(s, pk, P, x, M, topk_ids, w8, L, st));
+  if (rc != MOE_OK) return rc;
+  return launched(launch_down(s, pk, P, M, topk_ids, topk_w, out, w8, L, st));
+}
+
+int moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t M, int32_t* counts, int32_t* offsets,
+                int32_t* perm, void* ws, size_t ws_bytes, void* stream) {
+  Shape s;
+  int rc = check_cfg(cfg, &s);
+  if (rc != MOE_OK) return rc;
+  if (M < 0) return MOE_ERR_SHAPE;
+  if (!counts || !offsets || !ws || (M > 0 && (!topk_ids || !perm))) return MOE_ERR_NULL;
+  if (!aligned4(counts) || !aligned4(offsets) || !aligned4(perm) || !aligned4(topk_ids) || !aligned16(ws))
+    return MOE_ERR_ALIGN;
+  const WsLayout L = ws_layout(s.H, s.E, s.k, s.I, s.has_shared, 1);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  return launched(launch_permute(s, topk_ids, M, counts, offsets, perm,
+                                 reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + L.err),
+                                 static_cast<hipStream_t>(stream)));
+}
+
+int moe_get_device_error(void* ws, void* stream, int32_t* code_host) {
+  if (!ws || !code_host) return MOE_ERR_NULL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int32_t v = 0;
+  // the error word is the first word of every workspace layout
+  if (hipMemcpyAsync(&v, ws, sizeof v, hipMemcpyDeviceToHost, st) != hipSuccess) return MOE_ERR_LAUNCH;
+  if (hipStreamSynchronize(st) != hipSuccess) return MOE_ERR_LAUNCH;
+  *code_host = v;
+  if (v != 0) {
+    if (launch_fill_zero(ws, sizeof v, st) != hipSuccess) return MOE_ERR_LAUNCH;
+    if (hipStreamSynchronize(st) != hipSuccess) return MOE_ERR_LAUNCH;
+    return MOE_ERR_DEVICE;
+  }
+  return MOE_OK;
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case MOE_ERR_ALIGN: return "a pointer is not aligned (16 bytes for arrays, 4 for ids/weights)";
+    case MOE_ERR_WORKSPACE: return "workspace or packed buffer too small";
+    case MOE_ERR_UNSUPPORTED: return "no kernel is compiled for this shape";
+    case MOE_ERR_LAUNCH: return "the HIP runtime rejected a launch or copy";
+    case MOE_ERR_DEVICE: return "a device-side data error was recorded (expert id out of range)";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_build_info(void) {
+  return "arch=gfx950 layout=tile64-lanerow-v1 "
+         "route=wave-per-row-fp32+lastwg-topk "
+         "gate_up=int4-dot2bf16-sgpr-act(GW20P4|GW2P2)+shared-bf16(KS-split,lastwg) "
+         "down=int4-dot2bf16(GW6P2|GW1P1)+lastwg-combine "
+         "permute=1wg-stable-counting-sort "
+         "max_experts=512 max_decode_slots=4096";
+}
+
+}  // extern "C"

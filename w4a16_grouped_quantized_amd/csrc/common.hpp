@@ -1,0 +1,174 @@
+// common.hpp — device helpers and the workspace layout shared by the kernels
+// and the host entry points.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "layout.hpp"
+
+namespace moe {
+
+// Workspace: counters and the sticky error word first, then the per-call
+// scratch arrays, each 256-byte aligned.
+struct WsLayout {
+  size_t err, route_cnt, shgu_cnt, dn_cnt;   // int32 words
+  size_t logits;                             // fp32 [Mmax][E]
+  size_t h;                                  // bf16 [Mmax*k][I]
+  size_t h_sh;                               // bf16 [Mmax][I]
+  size_t shgu_part;                          // fp32 [Mmax][Tgu][KSgu][64]
+  size_t dpart;                              // fp32 [Mmax*k][H]
+  size_t shdn_part;                          // fp32 [Mmax][KSdn][H]
+  size_t total;
+  int Tgu, Tdn, KSgu, KSdn, CWgu, CWdn;
+};
+
+// The shared expert's K split targets the same bytes per wavefront as the
+// routed matrix of the same phase (its K-groups per wavefront).
+inline SharedSplit shared_gu_split(int H) { return shared_split_for(H, ksplit_for(H / kGroup).GW); }
+inline SharedSplit shared_dn_split(int I) { return shared_split_for(I, ksplit_for(I / kGroup).GW); }
+
+inline WsLayout ws_layout(int H, int E, int k, int I, int has_shared, int Mmax) {
+  WsLayout w;
+  w.Tgu = I / 32;
+  w.Tdn = H / 64;
+  SharedSplit sg = shared_gu_split(H);
+  SharedSplit sd = shared_dn_split(I);
+  w.KSgu = sg.KS; w.CWgu = sg.CW;
+  w.KSdn = sd.KS; w.CWdn = sd.CW;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+  w.err = take(4);
+  w.route_cnt = take(4);
+  w.shgu_cnt = take((size_t)4 * w.Tgu);
+  w.dn_cnt = take((size_t)4 * w.Tdn);
+  size_t M = (size_t)Mmax;
+  w.logits = take(M * E * 4);
+  w.h = take(M * k * I * 2 * 2);                  // (hi, lo) per value
+  w.h_sh = take(has_shared ? M * I * 2 * 2 : 0);
+  w.shgu_part = take(has_shared ? M * w.Tgu * w.KSgu * 64 * 4 : 0);
+  w.dpart = take(M * k * H * 4);
+  w.shdn_part = take(has_shared ? M * w.KSdn * H * 4 : 0);
+  w.total = off;
+  return w;
+}
+
+// ---------------------------------------------------------------- device helpers
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Activations read by whole wavefronts at uniform addresses go through the
+// constant address space, so they are fetched with scalar loads into SGPRs
+// (they are never written while a kernel reads them).
+typedef __attribute__((address_space(4))) const uint32_t* cptr32;
+__device__ __forceinline__ cptr32 as_scalar_ptr(const void* p) { return (cptr32)(p); }
+
+// bf16 (128, 128) in both halves, kept in a VGPR the compiler cannot fold, so
+// that (w & 0x000F000F) | magic becomes a single v_and_or_b32.
+__device__ __forceinline__ uint32_t bf16_pair_magic() {
+  uint32_t m;
+  asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(m));
+  return m;
+}
+
+// One 32-input group of a routed row against 16 dwords of bf16 activations:
+// returns init + sum_k (128 + u_k) * x_k.  With init = -136 * sum_k x_k this
+// is sum_k (u_k - 8) * x_k = sum_k q_k * x_k: every code is turned into the
+// exact bf16 value 128 + u by OR-ing it under the exponent of 128.
+__device__ __forceinline__ float dot_group_q4(uint4 w, cptr32 xg, float init, uint32_t magic) {
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+  float p = init;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t pair = ((wd[d] >> (4 * i)) & 0x000F000Fu) | magic;
+      p = dot2_bf16(pair, xg[4 * d + i], p);
+    }
+  }
+  return p;
+}
+
+// The same against an activation kept as a bf16 (hi, lo) pair, hi + lo
+// carrying ~16 significant bits: dwords 0..15 of xg hold hi, 16..31 lo.
+__device__ __forceinline__ float dot_group_q4_hilo(uint4 w, cptr32 xg, float init, uint32_t magic) {
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+  float p = init;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t pair = ((wd[d] >> (4 * i)) & 0x000F000Fu) | magic;
+      p = dot2_bf16(pair, xg[4 * d + i], p);
+      p = dot2_bf16(pair, xg[16 + 4 * d + i], p);
+    }
+  }
+  return p;
+}
+
+// An fp32 value as two bf16 whose sum carries ~16 significant bits; stored
+// as one group of 32 hi values followed by the group's 32 lo values.
+__device__ __forceinline__ void store_hilo(uint16_t* __restrict__ group_base, int i, float v) {
+  const uint16_t hi = f32_to_bf16(v);
+  const uint16_t lo = f32_to_bf16(v - bf16_to_f32(hi));
+  group_base[i] = hi;
+  group_base[32 + i] = lo;
+}
+
+// Eight bf16 weights (natural order) against 4 dwords of bf16 activations.
+__device__ __forceinline__ float dot_chunk_bf16(uint4 w, cptr32 xc, float acc) {
+  acc = dot2_bf16(w.x, xc[0], acc);
+  acc = dot2_bf16(w.y, xc[1], acc);
+  acc = dot2_bf16(w.z, xc[2], acc);
+  acc = dot2_bf16(w.w, xc[3], acc);
+  return acc;
+}
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Last-arriver protocol for data handed between workgroups of one launch
+// (they may sit on different XCDs, whose L2 caches are not coherent with each
+// other).  The barrier makes every wavefront's plain stores reach its L2;
+// thread 0 then releases them to agent scope (L2 write-back) and counts the
+// arrival.  The workgroup that arrives last acquires (L1/L2 invalidate), so
+// its plain loads that follow see every other workgroup's data, and resets
+// the counter for the next call.  Returns true in all threads of that
+// workgroup.
+__device__ __forceinline__ bool arrive_last(int* counter, int expected, int* lds_flag) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = (old == expected - 1);
+    if (last) {
+      __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    *lds_flag = last;
+  }
+  __syncthreads();
+  return *lds_flag != 0;
+}
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+}  // namespace moe

@@ -1,0 +1,486 @@
+// experts.hip — routed INT4 and shared BF16 expert FFNs for small token
+// counts (decode M = 1 and multi-token verify), plus the weighted combine.
+//
+// Two launches per call:
+//   k_gate_up: for every distinct routed expert of the call and every 64-row
+//              tile of its gate_up matrix, h = silu(W1 x) * (W3 x) for each
+//              (token, slot) routed to it; the shared expert's gate_up rows
+//              are extra workgroups (K split over KS workgroups, reduced by
+//              the last one to arrive).
+//   k_down:    for every distinct expert and 64-row tile of its down matrix,
+//              the per-slot partial rows W2 h; the shared down rows likewise;
+//              the last workgroup to finish a tile sums
+//              out[t][n] = sum_j w[t][j] * partial[t,j][n] + shared[t][n]
+//              in a fixed order (deterministic, no float atomics).
+//
+// Memory shape: one wavefront lane owns one weight row; each of the 4
+// wavefronts of a workgroup streams a contiguous run of K-groups with
+// coalesced 16-byte loads (1 KiB per wavefront load), all issued before any
+// math.  The activations of a group are wavefront-uniform and live in scalar
+// registers, so the VALU work per 16-byte chunk is 12 shifts/masks and 16
+// v_dot2_f32_bf16 with no cross-lane reduction.
+#include "launch.hpp"
+
+namespace moe {
+
+struct ExpArgs {
+  int M, E, k, H, I, S, has_shared;
+  int Tgu, Tdn, KSgu, KSdn;
+  const int32_t* __restrict__ ids;
+  const float* __restrict__ topk_w;
+  const uint16_t* __restrict__ x;
+  // packed weights
+  const uint8_t* __restrict__ gu_q;
+  const uint16_t* __restrict__ gu_s;
+  const uint8_t* __restrict__ dn_q;
+  const uint16_t* __restrict__ dn_s;
+  const uint16_t* __restrict__ sh_gu;
+  const uint16_t* __restrict__ sh_dn;
+  size_t gu_q_stride, gu_s_stride, dn_q_stride, dn_s_stride;  // bytes / elements (scales)
+  // workspace
+  int32_t* __restrict__ err;
+  int32_t* __restrict__ shgu_cnt;
+  int32_t* __restrict__ dn_cnt;
+  uint16_t* __restrict__ h;       // [S][I/32][hi 32 | lo 32]
+  uint16_t* __restrict__ h_sh;    // [M][I/32][hi 32 | lo 32]
+  float* __restrict__ shgu_part;  // [M][Tgu][KSgu][64]
+  float* __restrict__ dpart;      // [S][H]
+  float* __restrict__ shdn_part;  // [M][KSdn][H]
+  uint16_t* __restrict__ out;     // [M][H]
+};
+
+struct UnitLds {
+  int first[kMaxExperts];
+  int mem[kMaxSlots];
+  int wcnt[kWavesPerBlock];
+  int e, nmem, flag;
+  float red[kWavesPerBlock][kWave];
+  float bias[kMaxGroups];
+};
+
+// The u-th distinct valid expert of ids[0..S) in order of first occurrence,
+// and the list of slots routed to it (ascending).  Sets L.e = -1 if the call
+// has fewer than u+1 distinct experts.  Whole-workgroup call.
+__device__ void find_unit(const int32_t* __restrict__ ids, int S, int E, int u, UnitLds& L) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int e = tid; e < E; e += kBlock) L.first[e] = 0x7FFFFFFF;
+  if (tid == 0) { L.e = -1; L.nmem = 0; }
+  __syncthreads();
+  for (int p = tid; p < S; p += kBlock) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) atomicMin(&L.first[e], p);
+  }
+  __syncthreads();
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int running = 0;
+  for (int base = 0; base < S; base += kBlock) {
+    const int p = base + tid;
+    const int e = p < S ? ids[p] : -1;
+    const bool f = (e >= 0 && e < E) && L.first[e] == p;
+    const uint64_t bal = __ballot(f);
+    if (lane == 0) L.wcnt[wave] = __popcll(bal);
+    __syncthreads();
+    int before = running, total = running;
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+      if (w < wave) before += L.wcnt[w];
+      total += L.wcnt[w];
+    }
+    if (f && before + __popcll(bal & lt) == u) L.e = e;
+    running = total;
+    __syncthreads();
+    if (running > u) break;
+  }
+  const int eu = L.e;
+  if (eu < 0) return;
+  // members, in slot order
+  int count = 0;
+  for (int base = 0; base < S; base += kBlock) {
+    const int p = base + tid;
+    const bool m = p < S && ids[p] == eu;
+    const uint64_t bal = __ballot(m);
+    if (lane == 0) L.wcnt[wave] = __popcll(bal);
+    __syncthreads();
+    int before = count, total = count;
+    for (int w = 0; w < kWavesPerBlock; ++w) {
+      if (w < wave) before += L.wcnt[w];
+      total += L.wcnt[w];
+    }
+    if (m) L.mem[before + __popcll(bal & lt)] = p;
+    count = total;
+    __syncthreads();
+  }
+  if (tid == 0) L.nmem = count;
+  __syncthreads();
+}
+
+// P bf16 scales of one lane-load, as float.
+template <int P>
+struct ScalePack {
+  uint32_t w[(P + 1) / 2];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ p) {
+    if constexpr (P == 4) {
+      const uint2 v = *reinterpret_cast<const uint2*>(p);
+      w[0] = v.x; w[1] = v.y;
+    } else if constexpr (P == 2) {
+      w[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else {
+      w[0] = *p;
+    }
+  }
+  __device__ __forceinline__ float get(int q) const {
+    const uint32_t v = w[q >> 1];
+    return (q & 1) ? __uint_as_float(v & 0xFFFF0000u) : __uint_as_float(v << 16);
+  }
+};
+
+// -136 * (sum of the 32 values of group g of act): the correction that turns
+// sum (128 + u) * x into sum q * x.  Loaded by one lane per group.  With HILO
+// the group holds 32 hi then 32 lo bf16 values whose pairwise sums are the
+// activation, and the sum runs over all 64.
+template <bool HILO>
+struct GroupBias {
+  static constexpr int NV = HILO ? 8 : 4;
+  uint4 v[NV];
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ act, int g) {
+    const uint4* p = reinterpret_cast<const uint4*>(act + g * kGroup * (HILO ? 2 : 1));
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = p[i];
+  }
+  __device__ __forceinline__ float value() const {
+    const uint32_t one2 = 0x3F803F80u;  // bf16 (1.0, 1.0)
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      s = dot2_bf16(v[i].x, one2, s);
+      s = dot2_bf16(v[i].y, one2, s);
+      s = dot2_bf16(v[i].z, one2, s);
+      s = dot2_bf16(v[i].w, one2, s);
+    }
+    return -136.0f * s;
+  }
+};
+
+// One wavefront's K-run of a routed tile against one activation vector;
+// bias[g] holds the group corrections of that vector (LDS).  HILO: the
+// activation is stored as (hi, lo) bf16 groups (see store_hilo).
+template <int GW, int P, bool HILO>
+__device__ __forceinline__ float routed_dot(const uint4 (&wq)[GW], const ScalePack<P> (&sc)[GW / P],
+                                            const uint16_t* __restrict__ act, const float* bias, int g0,
+                                            uint32_t magic) {
+  const cptr32 a32 = as_scalar_ptr(act);
+  float acc = 0.f;
+#pragma unroll
+  for (int gi = 0; gi < GW; ++gi) {
+    // Opaque copy: keeps the code-pair extraction next to its dot products
+    // instead of letting it be hoisted out of the caller's token loop (which
+    // would hold 16 extracted pairs per group in VGPRs).
+    uint4 w = wq[gi];
+    asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+    float pr;
+    if constexpr (HILO) pr = dot_group_q4_hilo(w, a32 + (g0 + gi) * 32, bias[g0 + gi], magic);
+    else pr = dot_group_q4(w, a32 + (g0 + gi) * 16, bias[g0 + gi], magic);
+    acc = fmaf(sc[gi / P].get(gi % P), pr, acc);
+  }
+  return acc;
+}
+
+// Shared BF16 rows: CW chunks of 8 inputs from chunk c0 on.
+template <int CW, bool HILO>
+__device__ __forceinline__ float shared_dot(const uint4 (&wc)[CW], const uint16_t* __restrict__ act, int c0) {
+  const cptr32 a32 = as_scalar_ptr(act);
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < CW; ++c) {
+    if constexpr (HILO) {
+      const int cc = c0 + c;  // group cc / 4, quarter cc % 4
+      const cptr32 hi = a32 + (cc >> 2) * 32 + (cc & 3) * 4;
+      acc = dot_chunk_bf16(wc[c], hi, acc);
+      acc = dot_chunk_bf16(wc[c], hi + 16, acc);
+    } else {
+      acc = dot_chunk_bf16(wc[c], a32 + (c0 + c) * 4, acc);
+    }
+  }
+  return acc;
+}
+
+// --------------------------------------------------------------- gate_up
+
+template <int GW, int P, int CW>
+__global__ __launch_bounds__(kBlock) void k_gate_up(const ExpArgs a) {
+  __shared__ UnitLds L;
+  const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
+  const uint32_t magic = bf16_pair_magic();
+  const int GK = a.H / kGroup;
+  const int nrouted = a.S * a.Tgu;
+  const int blk = blockIdx.x;
+  if (blk < nrouted) {
+    const int u = blk / a.Tgu, b = blk % a.Tgu;
+    find_unit(a.ids, a.S, a.E, u, L);
+    const int e = L.e;
+    if (e < 0) return;
+    const int nmem = L.nmem;
+    const bool active = wave * GW < GK;
+    const int g0 = active ? wave * GW : 0;
+    // group corrections of the first column are requested before the weights
+    GroupBias<false> gb;
+    if (tid < GK) gb.load(a.x + (size_t)(uniform(L.mem[0]) / a.k) * a.H, tid);
+    uint4 wq[GW];
+    ScalePack<P> sc[GW / P];
+    const uint8_t* qb = a.gu_q + (size_t)e * a.gu_q_stride + ((size_t)(b * GK + g0) * kWave + lane) * 16;
+#pragma unroll
+    for (int i = 0; i < GW; ++i) wq[i] = *reinterpret_cast<const uint4*>(qb + (size_t)i * kWave * 16);
+    const uint16_t* sb = a.gu_s + (size_t)e * a.gu_s_stride + ((size_t)(b * (GK / P) + g0 / P) * kWave + lane) * P;
+#pragma unroll
+    for (int j = 0; j < GW / P; ++j) sc[j].load(sb + (size_t)j * kWave * P);
+    for (int c = 0; c < nmem; ++c) {
+      const int p = uniform(L.mem[c]);
+      const uint16_t* act = a.x + (size_t)(p / a.k) * a.H;
+      if (c > 0 && tid < GK) gb.load(act, tid);
+      if (tid < GK) L.bias[tid] = gb.value();
+      __syncthreads();
+      const float acc = active ? routed_dot<GW, P, false>(wq, sc, act, L.bias, g0, magic) : 0.f;
+      L.red[wave][lane] = acc;
+      __syncthreads();
+      if (tid < 32) {
+        float g = 0.f, up = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWavesPerBlock; ++w) { g += L.red[w][tid]; up += L.red[w][tid + 32]; }
+        // tile b's 32 outputs are exactly group b of h
+        store_hilo(a.h + ((size_t)p * a.I + 32 * b) * 2, tid, silu_f32(g) * up);
+      }
+      __syncthreads();
+    }
+    return;
+  }
+  if constexpr (CW == 0) {
+    return;  // no shared expert compiled into this variant
+  } else {
+  // shared expert: tile b, K slice ks
+  const int idx = blk - nrouted;
+  const int b = idx / a.KSgu, ks = idx % a.KSgu;
+  const int c0 = (ks * kWavesPerBlock + wave) * CW;  // first 8-input chunk of this wavefront
+  uint4 wc[CW];
+  const uint8_t* base = reinterpret_cast<const uint8_t*>(a.sh_gu) +
+                        ((size_t)(b * (a.H / 8) + c0) * kWave + lane) * 16;
+#pragma unroll
+  for (int c = 0; c < CW; ++c) wc[c] = *reinterpret_cast<const uint4*>(base + (size_t)c * kWave * 16);
+  for (int t = 0; t < a.M; ++t) {
+    L.red[wave][lane] = shared_dot<CW, false>(wc, a.x + (size_t)t * a.H, c0);
+    __syncthreads();
+    if (tid < kWave) {
+      float part = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) part += L.red[w][tid];
+      if (a.KSgu == 1) {
+        L.red[0][tid] = part;  // wave 0 owns row 0 of red after the sum
+      } else {
+        a.shgu_part[(((size_t)t * a.Tgu + b) * a.KSgu + ks) * kWave + tid] = part;
+      }
+    }
+    __syncthreads();
+    if (a.KSgu == 1 && tid < 32)
+      store_hilo(a.h_sh + ((size_t)t * a.I + 32 * b) * 2, tid, silu_f32(L.red[0][tid]) * L.red[0][tid + 32]);
+    __syncthreads();
+  }
+  if (a.KSgu == 1) return;
+  if (!arrive_last(&a.shgu_cnt[b], a.KSgu, &L.flag)) return;
+  for (int t = wave; t < a.M; t += kWavesPerBlock) {
+    float part = 0.f;
+    for (int s = 0; s < a.KSgu; ++s) part += a.shgu_part[(((size_t)t * a.Tgu + b) * a.KSgu + s) * kWave + lane];
+    const float up = __shfl_down(part, 32, 64);
+    if (lane < 32) store_hilo(a.h_sh + ((size_t)t * a.I + 32 * b) * 2, lane, silu_f32(part) * up);
+  }
+  }
+}
+
+// --------------------------------------------------------------- down + combine
+
+__device__ void combine_tile(const ExpArgs& a, int b) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = 64 * b + lane;
+  for (int t = wave; t < a.M; t += kWavesPerBlock) {
+    float y = 0.f;
+    for (int j = 0; j < a.k; ++j) {
+      const int p = t * a.k + j;
+      const int e = a.ids[p];
+      if (e < 0 || e >= a.E) {
+        if (lane == 0 && b == 0) atomicOr(a.err, 1);
+        continue;
+      }
+      y = fmaf(a.topk_w[p], a.dpart[(size_t)p * a.H + n], y);
+    }
+    if (a.has_shared)
+      for (int s = 0; s < a.KSdn; ++s) y += a.shdn_part[((size_t)t * a.KSdn + s) * a.H + n];
+    a.out[(size_t)t * a.H + n] = f32_to_bf16(y);
+  }
+}
+
+template <int GW, int P, int CW>
+__global__ __launch_bounds__(kBlock) void k_down(const ExpArgs a) {
+  __shared__ UnitLds L;
+  const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
+  const uint32_t magic = bf16_pair_magic();
+  const int GK = a.I / kGroup;
+  const int nrouted = a.S * a.Tdn;
+  const int expected = a.S + (a.has_shared ? a.KSdn : 0);
+  const int blk = blockIdx.x;
+  int b;
+  if (blk < nrouted) {
+    const int u = blk / a.Tdn;
+    b = blk % a.Tdn;
+    find_unit(a.ids, a.S, a.E, u, L);
+    const int e = L.e;
+    if (e >= 0) {
+      const int nmem = L.nmem;
+      const bool active = wave * GW < GK;
+      const int g0 = active ? wave * GW : 0;
+      GroupBias<true> gb;
+      if (tid < GK) gb.load(a.h + (size_t)uniform(L.mem[0]) * a.I * 2, tid);
+      uint4 wq[GW];
+      ScalePack<P> sc[GW / P];
+      const uint8_t* qb = a.dn_q + (size_t)e * a.dn_q_stride + ((size_t)(b * GK + g0) * kWave + lane) * 16;
+#pragma unroll
+      for (int i = 0; i < GW; ++i) wq[i] = *reinterpret_cast<const uint4*>(qb + (size_t)i * kWave * 16);
+      const uint16_t* sb = a.dn_s + (size_t)e * a.dn_s_stride + ((size_t)(b * (GK / P) + g0 / P) * kWave + lane) * P;
+#pragma unroll
+      for (int j = 0; j < GW / P; ++j) sc[j].load(sb + (size_t)j * kWave * P);
+      for (int c = 0; c < nmem; ++c) {
+        const int p = uniform(L.mem[c]);
+        const uint16_t* act = a.h + (size_t)p * a.I * 2;
+        if (c > 0 && tid < GK) gb.load(act, tid);
+        if (tid < GK) L.bias[tid] = gb.value();
+        __syncthreads();
+        const float acc = active ? routed_dot<GW, P, true>(wq, sc, act, L.bias, g0, magic) : 0.f;
+        L.red[wave][lane] = acc;
+        __syncthreads();
+        if (tid < kWave) {
+          float part = 0.f;
+#pragma unroll
+          for (int w = 0; w < kWavesPerBlock; ++w) part += L.red[w][tid];
+          a.dpart[(size_t)p * a.H + 64 * b + tid] = part;
+        }
+        __syncthreads();
+      }
+    }
+  } else if constexpr (CW == 0) {
+    return;  // no shared expert compiled into this variant (never launched)
+  } else {
+    const int idx = blk - nrouted;
+    b = idx / a.KSdn;
+    const int ks = idx % a.KSdn;
+    const int c0 = (ks * kWavesPerBlock + wave) * CW;
+    uint4 wc[CW];
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(a.sh_dn) +
+                          ((size_t)(b * (a.I / 8) + c0) * kWave + lane) * 16;
+#pragma unroll
+    for (int c = 0; c < CW; ++c) wc[c] = *reinterpret_cast<const uint4*>(base + (size_t)c * kWave * 16);
+    for (int t = 0; t < a.M; ++t) {
+      L.red[wave][lane] = shared_dot<CW, true>(wc, a.h_sh + (size_t)t * a.I * 2, c0);
+      __syncthreads();
+      if (tid < kWave) {
+        float part = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWavesPerBlock; ++w) part += L.red[w][tid];
+        a.shdn_part[((size_t)t * a.KSdn + ks) * a.H + 64 * b + tid] = part;
+      }
+      __syncthreads();
+    }
+  }
+  if (!arrive_last(&a.dn_cnt[b], expected, &L.flag)) return;
+  combine_tile(a, b);
+}
+
+// --------------------------------------------------------------- dispatch
+
+namespace {
+template <int GW, int P, int CW>
+hipError_t run_gate_up(const ExpArgs& a, hipStream_t st) {
+  const int grid = a.S * a.Tgu + (a.has_shared ? a.Tgu * a.KSgu : 0);
+  hipLaunchKernelGGL((k_gate_up<GW, P, CW>), dim3(grid), dim3(kBlock), 0, st, a);
+  return hipGetLastError();
+}
+template <int GW, int P, int CW>
+hipError_t run_down(const ExpArgs& a, hipStream_t st) {
+  const int grid = a.S * a.Tdn + (a.has_shared ? a.Tdn * a.KSdn : 0);
+  hipLaunchKernelGGL((k_down<GW, P, CW>), dim3(grid), dim3(kBlock), 0, st, a);
+  return hipGetLastError();
+}
+
+// Compiled (GW, P, CW) triples; CW is the shared expert's chunks per
+// wavefront (0 when there is no shared expert).
+//  gate_up: H=2560 -> 80 groups -> GW 20, P 4, CW 20;  H=256 -> GW 2, P 2, CW 2
+//  down:    I=768  -> 24 groups -> GW 6,  P 2, CW 6;   I=64  -> GW 1, P 1, CW 1
+struct Variant { int GW, P, CW; };
+}  // namespace
+
+static bool gu_variant(const Shape& s, Variant& v) {
+  const KSplit k = ksplit_for(s.H / kGroup);
+  const SharedSplit sh = shared_gu_split(s.H);
+  v = {k.GW, k.P, s.has_shared ? sh.CW : 0};
+  return (v.GW == 20 && v.P == 4 && (v.CW == 0 || v.CW == 20)) || (v.GW == 2 && v.P == 2 && (v.CW == 0 || v.CW == 2));
+}
+static bool dn_variant(const Shape& s, Variant& v) {
+  const KSplit k = ksplit_for(s.I / kGroup);
+  const SharedSplit sh = shared_dn_split(s.I);
+  v = {k.GW, k.P, s.has_shared ? sh.CW : 0};
+  return (v.GW == 6 && v.P == 2 && (v.CW == 0 || v.CW == 6)) || (v.GW == 1 && v.P == 1 && (v.CW == 0 || v.CW == 1));
+}
+
+bool experts_supported(const Shape& s) {
+  Variant a, b;
+  return gu_variant(s, a) && dn_variant(s, b);
+}
+
+static ExpArgs make_args(const Shape& s, const uint8_t* packed, const PackedLayout& PL, const uint16_t* x,
+                         int M, const int32_t* ids, const float* w, uint16_t* out, uint8_t* ws,
+                         const WsLayout& L) {
+  ExpArgs a;
+  a.M = M; a.E = s.E; a.k = s.k; a.H = s.H; a.I = s.I; a.S = M * s.k; a.has_shared = s.has_shared;
+  a.Tgu = L.Tgu; a.Tdn = L.Tdn; a.KSgu = L.KSgu; a.KSdn = L.KSdn;
+  a.ids = ids; a.topk_w = w; a.x = x;
+  a.gu_q = packed + PL.gu_q;
+  a.gu_s = reinterpret_cast<const uint16_t*>(packed + PL.gu_s);
+  a.dn_q = packed + PL.dn_q;
+  a.dn_s = reinterpret_cast<const uint16_t*>(packed + PL.dn_s);
+  a.sh_gu = reinterpret_cast<const uint16_t*>(packed + PL.sh_gu);
+  a.sh_dn = reinterpret_cast<const uint16_t*>(packed + PL.sh_dn);
+  a.gu_q_stride = PL.gu_q_stride; a.gu_s_stride = PL.gu_s_stride / 2;
+  a.dn_q_stride = PL.dn_q_stride; a.dn_s_stride = PL.dn_s_stride / 2;
+  a.err = reinterpret_cast<int32_t*>(ws + L.err);
+  a.shgu_cnt = reinterpret_cast<int32_t*>(ws + L.shgu_cnt);
+  a.dn_cnt = reinterpret_cast<int32_t*>(ws + L.dn_cnt);
+  a.h = reinterpret_cast<uint16_t*>(ws + L.h);
+  a.h_sh = reinterpret_cast<uint16_t*>(ws + L.h_sh);
+  a.shgu_part = reinterpret_cast<float*>(ws + L.shgu_part);
+  a.dpart = reinterpret_cast<float*>(ws + L.dpart);
+  a.shdn_part = reinterpret_cast<float*>(ws + L.shdn_part);
+  a.out = out;
+  return a;
+}
+
+hipError_t launch_gate_up(const Shape& s, const uint8_t* packed, const PackedLayout& PL, const uint16_t* x,
+                          int M, const int32_t* ids, uint8_t* ws, const WsLayout& L, hipStream_t st) {
+  const ExpArgs a = make_args(s, packed, PL, x, M, ids, nullptr, nullptr, ws, L);
+  Variant gv;
+  if (!gu_variant(s, gv)) return hipErrorInvalidValue;
+#define GU_CASE(GW_, P_, CW_) \
+  if (gv.GW == GW_ && gv.P == P_ && gv.CW == CW_) return run_gate_up<GW_, P_, CW_>(a, st);
+  GU_CASE(20, 4, 0) GU_CASE(20, 4, 20) GU_CASE(2, 2, 0) GU_CASE(2, 2, 2)
+#undef GU_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_down(const Shape& s, const uint8_t* packed, const PackedLayout& PL, int M,
+                       const int32_t* ids, const float* w, uint16_t* out, uint8_t* ws, const WsLayout& L,
+                       hipStream_t st) {
+  const ExpArgs a = make_args(s, packed, PL, nullptr, M, ids, w, out, ws, L);
+  Variant dv;
+  if (!dn_variant(s, dv)) return hipErrorInvalidValue;
+#define DN_CASE(GW_, P_, CW_) \
+  if (dv.GW == GW_ && dv.P == P_ && dv.CW == CW_) return run_down<GW_, P_, CW_>(a, st);
+  DN_CASE(6, 2, 0) DN_CASE(6, 2, 6) DN_CASE(1, 1, 0) DN_CASE(1, 1, 1)
+#undef DN_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

@@ -1,0 +1,47 @@
+// launch.hpp — host-side launchers of the kernels (one per .hip file).
+// Every launcher assumes its arguments were validated by the C-ABI layer and
+// returns the hipError_t of the launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace moe {
+
+constexpr int kMaxExperts = 512;   // LDS tables are sized for this
+constexpr int kMaxSlots = 4096;    // M * k handled by the decode (GEMV) kernels
+constexpr int kMaxTopK = 64;
+constexpr int kMaxGroups = 128;    // K/32 of the largest K (LDS group table)
+
+struct Shape {
+  int H, E, k, I, has_shared;
+};
+
+// routed/shared GEMV kernels: true if a kernel is compiled for this shape
+bool experts_supported(const Shape& s);
+bool route_supported(const Shape& s);
+
+hipError_t launch_route(const Shape& s, const float* router_w, const uint16_t* x, int M,
+                        bool rmsnorm, float eps, uint16_t* x_norm, int32_t* ids, float* w,
+                        uint8_t* ws, const WsLayout& L, hipStream_t st);
+
+// gate_up stage: h (routed, per slot) and h_sh (shared) into the workspace
+hipError_t launch_gate_up(const Shape& s, const uint8_t* packed, const PackedLayout& P, const uint16_t* x,
+                          int M, const int32_t* ids, uint8_t* ws, const WsLayout& L, hipStream_t st);
+// down stage + weighted combine: reads h / h_sh from the workspace
+hipError_t launch_down(const Shape& s, const uint8_t* packed, const PackedLayout& P, int M,
+                       const int32_t* ids, const float* w, uint16_t* out, uint8_t* ws, const WsLayout& L,
+                       hipStream_t st);
+
+hipError_t launch_permute(const Shape& s, const int32_t* ids, int M, int32_t* counts,
+                          int32_t* offsets, int32_t* perm, int32_t* err, hipStream_t st);
+
+hipError_t launch_pack(const Shape& s, const uint8_t* w13_q, const uint16_t* w13_s,
+                       const uint8_t* w2_q, const uint16_t* w2_s, const uint16_t* sh_w13,
+                       const uint16_t* sh_w2, uint8_t* packed, const PackedLayout& P,
+                       hipStream_t st);
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+
+}  // namespace moe

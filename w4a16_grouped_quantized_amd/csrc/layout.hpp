@@ -1,0 +1,107 @@
+// layout.hpp — the library's device layout of the expert weights, and the
+// work split every kernel and the packer agree on.  Host and device code.
+//
+// Routed INT4 matrices (per expert, W is N rows x K inputs, groups of 32):
+//   rows are taken in tiles of 64; one wavefront lane owns one row of a tile.
+//   gate_up (N = 2I): tile b holds gate rows 32b..32b+31 in lanes 0..31 and
+//     the matching up rows I+32b..I+32b+31 in lanes 32..63, so the SiLU*up
+//     product of a row pair never leaves the tile.
+//   down (N = H): tile b holds rows 64b..64b+63.
+//   codes: 16 bytes per (tile, group, lane) = the 32 codes of one row-group,
+//     at ((tile * K/32 + group) * 64 + lane) * 16.  Inside those 16 bytes,
+//     dword d covers inputs 8d..8d+7 of the group; nibble i (bits 4i..4i+3)
+//     holds input 8d+2i and nibble 4+i (bits 16+4i..) holds input 8d+2i+1,
+//     so (dword >> 4i) & 0x000F000F isolates the code pair of inputs
+//     (8d+2i, 8d+2i+1) in the two 16-bit halves.
+//   scales: bf16, P consecutive groups per lane and load:
+//     at ((tile * (K/32)/P + group/P) * 64 + lane) * P + group % P  (elements).
+// Shared BF16 matrices: tile b, chunk c of 8 inputs, lane l:
+//   16 bytes at ((tile * K/8 + c) * 64 + lane) * 16, inputs in natural order;
+//   same row-to-lane mapping as the routed matrices.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;   // 4 wavefronts per workgroup
+constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kGroup = 32;
+
+// How a workgroup's 4 wavefronts split the K/32 groups of one tile row-set:
+// W active wavefronts take GW consecutive groups each; scales are packed P
+// groups per lane-load with P dividing GW.
+struct KSplit {
+  int W, GW, P;
+};
+
+#if defined(__HIPCC__)
+__host__ __device__
+#endif
+inline KSplit ksplit_for(int groups) {
+  KSplit s;
+  s.W = (groups % 4 == 0) ? 4 : (groups % 2 == 0 ? 2 : 1);
+  s.GW = groups / s.W;
+  s.P = (s.GW % 4 == 0) ? 4 : (s.GW % 2 == 0 ? 2 : 1);
+  return s;
+}
+
+// Shared-expert K split: the K inputs of one tile are cut into KS slices
+// across workgroups, each slice into 4 wavefront ranges of CW chunks of 8.
+struct SharedSplit {
+  int KS, CW;
+};
+
+#if defined(__HIPCC__)
+__host__ __device__
+#endif
+inline SharedSplit shared_split_for(int K, int target_chunks_per_wave) {
+  SharedSplit s{1, K / 8 / kWavesPerBlock};
+  // largest KS with K/8/4 divisible by KS and chunks per wave >= target
+  for (int ks = 1; ks <= 16; ++ks) {
+    int chunks = K / 8 / kWavesPerBlock;
+    if (chunks % ks) continue;
+    if (chunks / ks < target_chunks_per_wave) break;
+    s.KS = ks;
+    s.CW = chunks / ks;
+  }
+  return s;
+}
+
+struct PackedLayout {
+  // byte offsets of each section inside the packed buffer
+  size_t gu_q, gu_s, dn_q, dn_s, sh_gu, sh_dn, total;
+  // per-expert strides in bytes
+  size_t gu_q_stride, gu_s_stride, dn_q_stride, dn_s_stride;
+};
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+#if defined(__HIPCC__)
+__host__ __device__
+#endif
+inline PackedLayout packed_layout(int H, int E, int I, int has_shared) {
+  PackedLayout L;
+  L.gu_q_stride = (size_t)2 * I * H / 2;
+  L.gu_s_stride = (size_t)2 * I * (H / kGroup) * 2;
+  L.dn_q_stride = (size_t)H * I / 2;
+  L.dn_s_stride = (size_t)H * (I / kGroup) * 2;
+  size_t off = 0;
+  L.gu_q = off; off = (off + L.gu_q_stride * E + 255) / 256 * 256;
+  L.gu_s = off; off = (off + L.gu_s_stride * E + 255) / 256 * 256;
+  L.dn_q = off; off = (off + L.dn_q_stride * E + 255) / 256 * 256;
+  L.dn_s = off; off = (off + L.dn_s_stride * E + 255) / 256 * 256;
+  L.sh_gu = off; if (has_shared) off = (off + (size_t)2 * I * H * 2 + 255) / 256 * 256;
+  L.sh_dn = off; if (has_shared) off = (off + (size_t)H * I * 2 + 255) / 256 * 256;
+  L.total = off;
+  return L;
+}
+
+// Row of matrix tile b served by lane l.
+#if defined(__HIPCC__)
+__host__ __device__
+#endif
+inline int gu_row(int b, int l, int I) { return l < 32 ? 32 * b + l : I + 32 * b + (l - 32); }
+
+}  // namespace moe

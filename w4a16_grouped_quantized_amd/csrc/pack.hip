@@ -1,0 +1,128 @@
+// pack.hip — one-time rearrangement of plain weights into the device layout
+// described in layout.hpp, and the workspace zero-fill.
+#include "launch.hpp"
+
+namespace moe {
+
+// One thread per 16-byte output chunk (tile, group, lane) of one expert.
+__global__ void k_pack_codes(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int E, int N,
+                             int K, int is_gu, int I, size_t stride) {
+  const int GK = K / kGroup, T = N / 64;
+  const size_t per_e = (size_t)T * GK * kWave;
+  const size_t total = per_e * E;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const int e = (int)(i / per_e);
+    const size_t r0 = i % per_e;
+    const int l = (int)(r0 % kWave);
+    const int g = (int)((r0 / kWave) % GK);
+    const int b = (int)(r0 / ((size_t)kWave * GK));
+    const int row = is_gu ? gu_row(b, l, I) : 64 * b + l;
+    const uint8_t* s = src + (size_t)e * stride + (size_t)row * (K / 2) + (size_t)g * 16;
+    uint32_t d[4];
+#pragma unroll
+    for (int dw = 0; dw < 4; ++dw) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t byte = s[4 * dw + q];  // codes of inputs 8dw+2q (low) and 8dw+2q+1 (high)
+        v |= (byte & 0xFu) << (4 * q);
+        v |= (byte >> 4) << (16 + 4 * q);
+      }
+      d[dw] = v;
+    }
+    *reinterpret_cast<uint4*>(dst + (size_t)e * stride + ((size_t)(b * GK + g) * kWave + l) * 16) =
+        make_uint4(d[0], d[1], d[2], d[3]);
+  }
+}
+
+// One thread per (tile, pack of P groups, lane) of one expert.
+__global__ void k_pack_scales(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int E, int N,
+                              int K, int is_gu, int I, int P, size_t stride_el) {
+  const int GK = K / kGroup, T = N / 64, NP = GK / P;
+  const size_t per_e = (size_t)T * NP * kWave;
+  const size_t total = per_e * E;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const int e = (int)(i / per_e);
+    const size_t r0 = i % per_e;
+    const int l = (int)(r0 % kWave);
+    const int gp = (int)((r0 / kWave) % NP);
+    const int b = (int)(r0 / ((size_t)kWave * NP));
+    const int row = is_gu ? gu_row(b, l, I) : 64 * b + l;
+    const uint16_t* s = src + (size_t)e * stride_el + (size_t)row * GK + (size_t)gp * P;
+    uint16_t* d = dst + (size_t)e * stride_el + ((size_t)(b * NP + gp) * kWave + l) * P;
+    for (int q = 0; q < P; ++q) d[q] = s[q];
+  }
+}
+
+// Shared BF16 matrix: one thread per (tile, chunk of 8 inputs, lane).
+__global__ void k_pack_bf16(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int N, int K,
+                            int is_gu, int I) {
+  const int T = N / 64, C = K / 8;
+  const size_t total = (size_t)T * C * kWave;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const int l = (int)(i % kWave);
+    const int c = (int)((i / kWave) % C);
+    const int b = (int)(i / ((size_t)kWave * C));
+    const int row = is_gu ? gu_row(b, l, I) : 64 * b + l;
+    const uint4 v = *reinterpret_cast<const uint4*>(src + (size_t)row * K + (size_t)c * 8);
+    *reinterpret_cast<uint4*>(dst + ((size_t)(b * C + c) * kWave + l) * 8) = v;
+  }
+}
+
+__global__ void k_fill_zero(uint4* __restrict__ p, size_t n16, uint8_t* __restrict__ tail, size_t ntail) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+  if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0;
+}
+
+static int grid_for(size_t n) {
+  size_t g = (n + 255) / 256;
+  if (g > 65536) g = 65536;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+hipError_t launch_pack(const Shape& s, const uint8_t* w13_q, const uint16_t* w13_s,
+                       const uint8_t* w2_q, const uint16_t* w2_s, const uint16_t* sh_w13,
+                       const uint16_t* sh_w2, uint8_t* packed, const PackedLayout& P,
+                       hipStream_t st) {
+  const int H = s.H, I = s.I, E = s.E;
+  const KSplit kg = ksplit_for(H / kGroup), kd = ksplit_for(I / kGroup);
+  hipError_t err;
+  size_t n = (size_t)E * (2 * I / 64) * (H / kGroup) * kWave;
+  hipLaunchKernelGGL(k_pack_codes, dim3(grid_for(n)), dim3(256), 0, st, w13_q, packed + P.gu_q, E, 2 * I, H, 1, I,
+                     P.gu_q_stride);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  n = (size_t)E * (2 * I / 64) * (H / kGroup / kg.P) * kWave;
+  hipLaunchKernelGGL(k_pack_scales, dim3(grid_for(n)), dim3(256), 0, st, w13_s,
+                     reinterpret_cast<uint16_t*>(packed + P.gu_s), E, 2 * I, H, 1, I, kg.P, P.gu_s_stride / 2);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  n = (size_t)E * (H / 64) * (I / kGroup) * kWave;
+  hipLaunchKernelGGL(k_pack_codes, dim3(grid_for(n)), dim3(256), 0, st, w2_q, packed + P.dn_q, E, H, I, 0, I,
+                     P.dn_q_stride);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  n = (size_t)E * (H / 64) * (I / kGroup / kd.P) * kWave;
+  hipLaunchKernelGGL(k_pack_scales, dim3(grid_for(n)), dim3(256), 0, st, w2_s,
+                     reinterpret_cast<uint16_t*>(packed + P.dn_s), E, H, I, 0, I, kd.P, P.dn_s_stride / 2);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (s.has_shared) {
+    n = (size_t)(2 * I / 64) * (H / 8) * kWave;
+    hipLaunchKernelGGL(k_pack_bf16, dim3(grid_for(n)), dim3(256), 0, st, sh_w13,
+                       reinterpret_cast<uint16_t*>(packed + P.sh_gu), 2 * I, H, 1, I);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    n = (size_t)(H / 64) * (I / 8) * kWave;
+    hipLaunchKernelGGL(k_pack_bf16, dim3(grid_for(n)), dim3(256), 0, st, sh_w2,
+                       reinterpret_cast<uint16_t*>(packed + P.sh_dn), H, I, 0, I);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
+  const size_t n16 = bytes / 16, tail = bytes % 16;
+  hipLaunchKernelGGL(k_fill_zero, dim3(grid_for(n16)), dim3(256), 0, st, reinterpret_cast<uint4*>(p), n16,
+                     reinterpret_cast<uint8_t*>(p) + n16 * 16, tail);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -178,6 +178,13 @@ def make_layer(shape: LayerShape, seed: int, return_q: bool = False, threads: in
     return Layer(shape, seed, router, w13_q, w13_s, w2_q, w2_s, sh13, sh2, q13, q2)
 
 
+def make_router(shape: LayerShape, seed: int) -> np.ndarray:
+    """The router of layer `seed` alone (same values make_layer draws)."""
+    d, _ = _seeds(seed, shape)
+    rng = np.random.Generator(np.random.PCG64(d["router"]))
+    return (rng.standard_normal((shape.n_experts, shape.hidden)) * 0.02).astype(np.float32)
+
+
 def make_tokens(shape: LayerShape, seed: int, M: int) -> np.ndarray:
     """x: bf16 bit patterns [M][H], bf16(N(0,1))."""
     d, _ = _seeds(seed, shape)
