@@ -88,7 +88,7 @@ __device__ __forceinline__ uint32_t bf16_pair_magic() {
 // returns init + sum_k (128 + u_k) * x_k.  With init = -136 * sum_k x_k this
 // is sum_k (u_k - 8) * x_k = sum_k q_k * x_k: every code is turned into the
 // exact bf16 value 128 + u by OR-ing it under the exponent of 128.
-__device__ __forceinline__ float dot_group_q4(uint4 w, cptr32 xg, float init, uint32_t magic) {
+__device__ __forceinline__ float dot_group_q4(uint4 w, const uint32_t* xg, float init, uint32_t magic) {
   const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
   float p = init;
 #pragma unroll
@@ -104,7 +104,7 @@ __device__ __forceinline__ float dot_group_q4(uint4 w, cptr32 xg, float init, ui
 
 // The same against an activation kept as a bf16 (hi, lo) pair, hi + lo
 // carrying ~16 significant bits: dwords 0..15 of xg hold hi, 16..31 lo.
-__device__ __forceinline__ float dot_group_q4_hilo(uint4 w, cptr32 xg, float init, uint32_t magic) {
+__device__ __forceinline__ float dot_group_q4_hilo(uint4 w, const uint32_t* xg, float init, uint32_t magic) {
   const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
   float p = init;
 #pragma unroll
@@ -129,7 +129,7 @@ __device__ __forceinline__ void store_hilo(uint16_t* __restrict__ group_base, in
 }
 
 // Eight bf16 weights (natural order) against 4 dwords of bf16 activations.
-__device__ __forceinline__ float dot_chunk_bf16(uint4 w, cptr32 xc, float acc) {
+__device__ __forceinline__ float dot_chunk_bf16(uint4 w, const uint32_t* xc, float acc) {
   acc = dot2_bf16(w.x, xc[0], acc);
   acc = dot2_bf16(w.y, xc[1], acc);
   acc = dot2_bf16(w.z, xc[2], acc);
@@ -145,24 +145,32 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Last-arriver protocol for data handed between workgroups of one launch
-// (they may sit on different XCDs, whose L2 caches are not coherent with each
-// other).  The barrier makes every wavefront's plain stores reach its L2;
-// thread 0 then releases them to agent scope (L2 write-back) and counts the
-// arrival.  The workgroup that arrives last acquires (L1/L2 invalidate), so
-// its plain loads that follow see every other workgroup's data, and resets
-// the counter for the next call.  Returns true in all threads of that
-// workgroup.
+// Data handed between workgroups of one launch.  They may sit on different
+// XCDs, whose L2 caches are not coherent with each other, and an agent-scope
+// release fence (a full L2 write-back) per workgroup costs several
+// microseconds per launch on this part.  So the data itself travels with
+// agent-coherent accesses: stores write through to the coherent level, loads
+// read from it, and the only ordering needed is that a producer's stores have
+// completed before its arrival is counted.
+__device__ __forceinline__ void st_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Last-arriver protocol: each thread waits for its own coherent stores to
+// complete (s_waitcnt 0), the barrier gathers the workgroup, thread 0 counts
+// the arrival.  The workgroup that arrives last sees every other
+// workgroup's coherent stores, resets the counter for the next call and gets
+// true in all its threads.  Loads that follow must be ld_coherent.
 __device__ __forceinline__ bool arrive_last(int* counter, int expected, int* lds_flag) {
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int last = (old == expected - 1);
-    if (last) {
-      __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    }
+    if (last) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *lds_flag = last;
   }
   __syncthreads();
@@ -170,5 +178,15 @@ __device__ __forceinline__ bool arrive_last(int* counter, int expected, int* lds
 }
 
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses,
+// not for its in-flight global loads (a plain __syncthreads also waits for
+// outstanding global memory operations, which would stall every wavefront
+// until most of its weight stream had landed).
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 }  // namespace moe

@@ -58,19 +58,52 @@ struct UnitLds {
   float bias[kMaxGroups];
 };
 
-// The u-th distinct valid expert of ids[0..S) in order of first occurrence,
-// and the list of slots routed to it (ascending).  Sets L.e = -1 if the call
-// has fewer than u+1 distinct experts.  Whole-workgroup call.
-__device__ void find_unit(const int32_t* __restrict__ ids, int S, int E, int u, UnitLds& L) {
+// The distinct valid experts of ids[0..S) are numbered in order of first
+// occurrence; a workgroup serving unit u needs that expert and the slots
+// routed to it (ascending).
+struct Unit {
+  int e;          // -1 when the call has fewer than u + 1 distinct experts
+  int nmem;
+  uint64_t mask;  // member slots as bits (S <= 64)
+};
+
+// S <= 64: every wavefront finds the unit on its own with cross-lane reads
+// (no LDS, no barrier).  Lane p holds slot p.
+__device__ __forceinline__ Unit find_unit_wave(const int32_t* __restrict__ ids, int S, int E, int u, int lane) {
+  const int id = lane < S ? ids[lane] : -1;
+  const bool valid = id >= 0 && id < E;
+  bool first = valid;
+  for (int q = 0; q < S; ++q) {
+    const int v = __builtin_amdgcn_readlane(id, q);
+    first = first && !(q < lane && v == id);
+  }
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const uint64_t fb = __ballot(first);
+  const int rank = __popcll(fb & lt);
+  const uint64_t sel = __ballot(first && rank == u);
+  Unit U;
+  if (sel == 0) {
+    U.e = -1; U.nmem = 0; U.mask = 0;
+    return U;
+  }
+  U.e = __builtin_amdgcn_readlane(id, __ffsll((unsigned long long)sel) - 1);
+  U.mask = __ballot(valid && id == U.e);
+  U.nmem = __popcll(U.mask);
+  return U;
+}
+
+// Any S (<= kMaxSlots): the workgroup builds a first-occurrence table and the
+// member list in LDS.  Whole-workgroup call.
+__device__ void find_unit_lds(const int32_t* __restrict__ ids, int S, int E, int u, UnitLds& L) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   for (int e = tid; e < E; e += kBlock) L.first[e] = 0x7FFFFFFF;
   if (tid == 0) { L.e = -1; L.nmem = 0; }
-  __syncthreads();
+  lds_sync();
   for (int p = tid; p < S; p += kBlock) {
     const int e = ids[p];
     if (e >= 0 && e < E) atomicMin(&L.first[e], p);
   }
-  __syncthreads();
+  lds_sync();
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int running = 0;
   for (int base = 0; base < S; base += kBlock) {
@@ -79,7 +112,7 @@ __device__ void find_unit(const int32_t* __restrict__ ids, int S, int E, int u, 
     const bool f = (e >= 0 && e < E) && L.first[e] == p;
     const uint64_t bal = __ballot(f);
     if (lane == 0) L.wcnt[wave] = __popcll(bal);
-    __syncthreads();
+    lds_sync();
     int before = running, total = running;
     for (int w = 0; w < kWavesPerBlock; ++w) {
       if (w < wave) before += L.wcnt[w];
@@ -87,19 +120,18 @@ __device__ void find_unit(const int32_t* __restrict__ ids, int S, int E, int u, 
     }
     if (f && before + __popcll(bal & lt) == u) L.e = e;
     running = total;
-    __syncthreads();
+    lds_sync();
     if (running > u) break;
   }
   const int eu = L.e;
   if (eu < 0) return;
-  // members, in slot order
   int count = 0;
   for (int base = 0; base < S; base += kBlock) {
     const int p = base + tid;
     const bool m = p < S && ids[p] == eu;
     const uint64_t bal = __ballot(m);
     if (lane == 0) L.wcnt[wave] = __popcll(bal);
-    __syncthreads();
+    lds_sync();
     int before = count, total = count;
     for (int w = 0; w < kWavesPerBlock; ++w) {
       if (w < wave) before += L.wcnt[w];
@@ -107,10 +139,29 @@ __device__ void find_unit(const int32_t* __restrict__ ids, int S, int E, int u, 
     }
     if (m) L.mem[before + __popcll(bal & lt)] = p;
     count = total;
-    __syncthreads();
+    lds_sync();
   }
   if (tid == 0) L.nmem = count;
-  __syncthreads();
+  lds_sync();
+}
+
+__device__ __forceinline__ Unit find_unit(const int32_t* __restrict__ ids, int S, int E, int u, UnitLds& L) {
+  if (S <= kWave) return find_unit_wave(ids, S, E, u, threadIdx.x & 63);
+  find_unit_lds(ids, S, E, u, L);
+  Unit U;
+  U.e = L.e; U.nmem = L.nmem; U.mask = 0;
+  return U;
+}
+
+// Slot of member c (called with c = 0, 1, ... in order; `m` carries the
+// remaining mask between calls when S <= 64).
+__device__ __forceinline__ int member_slot(int S, int c, uint64_t& m, const UnitLds& L) {
+  if (S <= kWave) {
+    const int p = __ffsll((unsigned long long)m) - 1;
+    m &= m - 1;
+    return p;
+  }
+  return uniform(L.mem[c]);
 }
 
 // P bf16 scales of one lane-load, as float.
@@ -162,24 +213,48 @@ struct GroupBias {
 
 // One wavefront's K-run of a routed tile against one activation vector;
 // bias[g] holds the group corrections of that vector (LDS).  HILO: the
-// activation is stored as (hi, lo) bf16 groups (see store_hilo).
+// activation is stored as (hi, lo) bf16 groups (see store_hilo).  The
+// activation dwords of B groups are fetched with one batch of scalar loads
+// (scalar loads return out of order, so each batch costs one full wait).
 template <int GW, int P, bool HILO>
 __device__ __forceinline__ float routed_dot(const uint4 (&wq)[GW], const ScalePack<P> (&sc)[GW / P],
                                             const uint16_t* __restrict__ act, const float* bias, int g0,
                                             uint32_t magic) {
-  const cptr32 a32 = as_scalar_ptr(act);
-  float acc = 0.f;
+  constexpr int DW = HILO ? 32 : 16;  // activation dwords per group
+  constexpr int B = HILO ? 1 : 2;     // groups per scalar-load batch
+  float acc = 0.f, lag1 = 0.f, lag2 = 0.f;
 #pragma unroll
-  for (int gi = 0; gi < GW; ++gi) {
-    // Opaque copy: keeps the code-pair extraction next to its dot products
-    // instead of letting it be hoisted out of the caller's token loop (which
-    // would hold 16 extracted pairs per group in VGPRs).
-    uint4 w = wq[gi];
-    asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
-    float pr;
-    if constexpr (HILO) pr = dot_group_q4_hilo(w, a32 + (g0 + gi) * 32, bias[g0 + gi], magic);
-    else pr = dot_group_q4(w, a32 + (g0 + gi) * 16, bias[g0 + gi], magic);
-    acc = fmaf(sc[gi / P].get(gi % P), pr, acc);
+  for (int g = 0; g < GW; g += B) {
+    // The batch address passes through an empty asm that also consumes the
+    // accumulator as it stood two batches earlier: the loads of batch i can
+    // start once batch i-2 is done, i.e. one batch of scalar prefetch, and
+    // the compiler cannot hoist all of them (they would not fit in SGPRs).
+    uint64_t addr = reinterpret_cast<uint64_t>(act) + (uint64_t)(g0 + g) * DW * 4;
+    addr = ((uint64_t)(uint32_t)uniform((int)(addr >> 32)) << 32) | (uint32_t)uniform((int)(uint32_t)addr);
+    asm volatile("" : "+s"(addr) : "v"(lag2));
+    const cptr32 xb = as_scalar_ptr(reinterpret_cast<const void*>(addr));
+    uint32_t xs[B][DW];
+#pragma unroll
+    for (int bb = 0; bb < B; ++bb)
+#pragma unroll
+      for (int i = 0; i < DW; ++i) xs[bb][i] = (g + bb < GW) ? xb[bb * DW + i] : 0u;
+#pragma unroll
+    for (int bb = 0; bb < B; ++bb) {
+      const int gi = g + bb;
+      if (gi < GW) {
+        // Opaque copy: keeps the code-pair extraction next to its dot
+        // products instead of letting it be hoisted out of the caller's
+        // token loop (16 extracted pairs per group would stay in VGPRs).
+        uint4 w = wq[gi];
+        asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+        float pr;
+        if constexpr (HILO) pr = dot_group_q4_hilo(w, xs[bb], bias[g0 + gi], magic);
+        else pr = dot_group_q4(w, xs[bb], bias[g0 + gi], magic);
+        acc = fmaf(sc[gi / P].get(gi % P), pr, acc);
+      }
+    }
+    lag2 = lag1;
+    lag1 = acc;
   }
   return acc;
 }
@@ -191,13 +266,18 @@ __device__ __forceinline__ float shared_dot(const uint4 (&wc)[CW], const uint16_
   float acc = 0.f;
 #pragma unroll
   for (int c = 0; c < CW; ++c) {
+    uint32_t xs[HILO ? 8 : 4];
     if constexpr (HILO) {
       const int cc = c0 + c;  // group cc / 4, quarter cc % 4
       const cptr32 hi = a32 + (cc >> 2) * 32 + (cc & 3) * 4;
-      acc = dot_chunk_bf16(wc[c], hi, acc);
-      acc = dot_chunk_bf16(wc[c], hi + 16, acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { xs[i] = hi[i]; xs[4 + i] = hi[16 + i]; }
+      acc = dot_chunk_bf16(wc[c], xs, acc);
+      acc = dot_chunk_bf16(wc[c], xs + 4, acc);
     } else {
-      acc = dot_chunk_bf16(wc[c], a32 + (c0 + c) * 4, acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xs[i] = a32[(c0 + c) * 4 + i];
+      acc = dot_chunk_bf16(wc[c], xs, acc);
     }
   }
   return acc;
@@ -215,15 +295,16 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(const ExpArgs a) {
   const int blk = blockIdx.x;
   if (blk < nrouted) {
     const int u = blk / a.Tgu, b = blk % a.Tgu;
-    find_unit(a.ids, a.S, a.E, u, L);
-    const int e = L.e;
-    if (e < 0) return;
-    const int nmem = L.nmem;
+    const Unit U = find_unit(a.ids, a.S, a.E, u, L);
+    if (U.e < 0) return;
+    const int e = U.e;
+    uint64_t m = U.mask;
     const bool active = wave * GW < GK;
     const int g0 = active ? wave * GW : 0;
-    // group corrections of the first column are requested before the weights
+    // the first column's group corrections are requested before the weights
+    int p = member_slot(a.S, 0, m, L);
     GroupBias<false> gb;
-    if (tid < GK) gb.load(a.x + (size_t)(uniform(L.mem[0]) / a.k) * a.H, tid);
+    if (tid < GK) gb.load(a.x + (size_t)(p / a.k) * a.H, tid);
     uint4 wq[GW];
     ScalePack<P> sc[GW / P];
     const uint8_t* qb = a.gu_q + (size_t)e * a.gu_q_stride + ((size_t)(b * GK + g0) * kWave + lane) * 16;
@@ -232,15 +313,16 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(const ExpArgs a) {
     const uint16_t* sb = a.gu_s + (size_t)e * a.gu_s_stride + ((size_t)(b * (GK / P) + g0 / P) * kWave + lane) * P;
 #pragma unroll
     for (int j = 0; j < GW / P; ++j) sc[j].load(sb + (size_t)j * kWave * P);
-    for (int c = 0; c < nmem; ++c) {
-      const int p = uniform(L.mem[c]);
+    for (int c = 0; c < U.nmem; ++c) {
+      if (c > 0) {
+        p = member_slot(a.S, c, m, L);
+        if (tid < GK) gb.load(a.x + (size_t)(p / a.k) * a.H, tid);
+      }
       const uint16_t* act = a.x + (size_t)(p / a.k) * a.H;
-      if (c > 0 && tid < GK) gb.load(act, tid);
       if (tid < GK) L.bias[tid] = gb.value();
-      __syncthreads();
-      const float acc = active ? routed_dot<GW, P, false>(wq, sc, act, L.bias, g0, magic) : 0.f;
-      L.red[wave][lane] = acc;
-      __syncthreads();
+      lds_sync();
+      L.red[wave][lane] = active ? routed_dot<GW, P, false>(wq, sc, act, L.bias, g0, magic) : 0.f;
+      lds_sync();
       if (tid < 32) {
         float g = 0.f, up = 0.f;
 #pragma unroll
@@ -248,71 +330,95 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(const ExpArgs a) {
         // tile b's 32 outputs are exactly group b of h
         store_hilo(a.h + ((size_t)p * a.I + 32 * b) * 2, tid, silu_f32(g) * up);
       }
-      __syncthreads();
+      lds_sync();
     }
     return;
   }
   if constexpr (CW == 0) {
     return;  // no shared expert compiled into this variant
   } else {
-  // shared expert: tile b, K slice ks
-  const int idx = blk - nrouted;
-  const int b = idx / a.KSgu, ks = idx % a.KSgu;
-  const int c0 = (ks * kWavesPerBlock + wave) * CW;  // first 8-input chunk of this wavefront
-  uint4 wc[CW];
-  const uint8_t* base = reinterpret_cast<const uint8_t*>(a.sh_gu) +
-                        ((size_t)(b * (a.H / 8) + c0) * kWave + lane) * 16;
+    // shared expert: tile b, K slice ks
+    const int idx = blk - nrouted;
+    const int b = idx / a.KSgu, ks = idx % a.KSgu;
+    const int c0 = (ks * kWavesPerBlock + wave) * CW;  // first 8-input chunk of this wavefront
+    uint4 wc[CW];
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(a.sh_gu) +
+                          ((size_t)(b * (a.H / 8) + c0) * kWave + lane) * 16;
 #pragma unroll
-  for (int c = 0; c < CW; ++c) wc[c] = *reinterpret_cast<const uint4*>(base + (size_t)c * kWave * 16);
-  for (int t = 0; t < a.M; ++t) {
-    L.red[wave][lane] = shared_dot<CW, false>(wc, a.x + (size_t)t * a.H, c0);
-    __syncthreads();
-    if (tid < kWave) {
+    for (int c = 0; c < CW; ++c) wc[c] = *reinterpret_cast<const uint4*>(base + (size_t)c * kWave * 16);
+    for (int t = 0; t < a.M; ++t) {
+      L.red[wave][lane] = shared_dot<CW, false>(wc, a.x + (size_t)t * a.H, c0);
+      lds_sync();
+      if (tid < kWave) {
+        float part = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWavesPerBlock; ++w) part += L.red[w][tid];
+        if (a.KSgu == 1) L.red[0][tid] = part;
+        else st_coherent(&a.shgu_part[(((size_t)t * a.Tgu + b) * a.KSgu + ks) * kWave + tid], part);
+      }
+      lds_sync();
+      if (a.KSgu == 1 && tid < 32)
+        store_hilo(a.h_sh + ((size_t)t * a.I + 32 * b) * 2, tid, silu_f32(L.red[0][tid]) * L.red[0][tid + 32]);
+      lds_sync();
+    }
+    if (a.KSgu == 1) return;
+    if (!arrive_last(&a.shgu_cnt[b], a.KSgu, &L.flag)) return;
+    for (int t = wave; t < a.M; t += kWavesPerBlock) {
+      float pv[kMaxKSplit];
+#pragma unroll
+      for (int s2 = 0; s2 < kMaxKSplit; ++s2)
+        pv[s2] = s2 < a.KSgu ? ld_coherent(&a.shgu_part[(((size_t)t * a.Tgu + b) * a.KSgu + s2) * kWave + lane]) : 0.f;
       float part = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWavesPerBlock; ++w) part += L.red[w][tid];
-      if (a.KSgu == 1) {
-        L.red[0][tid] = part;  // wave 0 owns row 0 of red after the sum
-      } else {
-        a.shgu_part[(((size_t)t * a.Tgu + b) * a.KSgu + ks) * kWave + tid] = part;
-      }
+      for (int s2 = 0; s2 < kMaxKSplit; ++s2) part += pv[s2];
+      const float up = __shfl_down(part, 32, 64);
+      if (lane < 32) store_hilo(a.h_sh + ((size_t)t * a.I + 32 * b) * 2, lane, silu_f32(part) * up);
     }
-    __syncthreads();
-    if (a.KSgu == 1 && tid < 32)
-      store_hilo(a.h_sh + ((size_t)t * a.I + 32 * b) * 2, tid, silu_f32(L.red[0][tid]) * L.red[0][tid + 32]);
-    __syncthreads();
-  }
-  if (a.KSgu == 1) return;
-  if (!arrive_last(&a.shgu_cnt[b], a.KSgu, &L.flag)) return;
-  for (int t = wave; t < a.M; t += kWavesPerBlock) {
-    float part = 0.f;
-    for (int s = 0; s < a.KSgu; ++s) part += a.shgu_part[(((size_t)t * a.Tgu + b) * a.KSgu + s) * kWave + lane];
-    const float up = __shfl_down(part, 32, 64);
-    if (lane < 32) store_hilo(a.h_sh + ((size_t)t * a.I + 32 * b) * 2, lane, silu_f32(part) * up);
-  }
   }
 }
 
 // --------------------------------------------------------------- down + combine
 
+// out[t][n] = sum_j w[t][j] * partial[t*k+j][n] + sum_s shared_part[t][s][n],
+// for the 64 rows n of tile b; slots with an invalid id add nothing.  All
+// loads of a block of 8 slots are issued before any of them is used (the
+// partial of every slot is in bounds; an invalid slot's is discarded by a
+// select, never multiplied in).
 __device__ void combine_tile(const ExpArgs& a, int b) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = 64 * b + lane;
+  bool bad = false;
   for (int t = wave; t < a.M; t += kWavesPerBlock) {
     float y = 0.f;
-    for (int j = 0; j < a.k; ++j) {
-      const int p = t * a.k + j;
-      const int e = a.ids[p];
-      if (e < 0 || e >= a.E) {
-        if (lane == 0 && b == 0) atomicOr(a.err, 1);
-        continue;
+    for (int j0 = 0; j0 < a.k; j0 += 8) {
+      int ev[8];
+      float pv[8], wv[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int p = t * a.k + j0 + jj;
+        const bool in = j0 + jj < a.k;
+        ev[jj] = in ? a.ids[p] : 0;
+        wv[jj] = in ? a.topk_w[p] : 0.f;
+        pv[jj] = in ? ld_coherent(&a.dpart[(size_t)p * a.H + n]) : 0.f;
       }
-      y = fmaf(a.topk_w[p], a.dpart[(size_t)p * a.H + n], y);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const bool ok = ev[jj] >= 0 && ev[jj] < a.E;
+        bad = bad || (j0 + jj < a.k && !ok);
+        y = ok ? fmaf(wv[jj], pv[jj], y) : y;
+      }
     }
-    if (a.has_shared)
-      for (int s = 0; s < a.KSdn; ++s) y += a.shdn_part[((size_t)t * a.KSdn + s) * a.H + n];
+    if (a.has_shared) {
+      float sv[kMaxKSplit];
+#pragma unroll
+      for (int s2 = 0; s2 < kMaxKSplit; ++s2)
+        sv[s2] = s2 < a.KSdn ? ld_coherent(&a.shdn_part[((size_t)t * a.KSdn + s2) * a.H + n]) : 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < kMaxKSplit; ++s2) y += sv[s2];
+    }
     a.out[(size_t)t * a.H + n] = f32_to_bf16(y);
   }
+  if (bad && b == 0 && lane == 0) atomicOr(a.err, 1);
 }
 
 template <int GW, int P, int CW>
@@ -328,14 +434,15 @@ __global__ __launch_bounds__(kBlock) void k_down(const ExpArgs a) {
   if (blk < nrouted) {
     const int u = blk / a.Tdn;
     b = blk % a.Tdn;
-    find_unit(a.ids, a.S, a.E, u, L);
-    const int e = L.e;
-    if (e >= 0) {
-      const int nmem = L.nmem;
+    const Unit U = find_unit(a.ids, a.S, a.E, u, L);
+    if (U.e >= 0) {
+      const int e = U.e;
+      uint64_t m = U.mask;
       const bool active = wave * GW < GK;
       const int g0 = active ? wave * GW : 0;
+      int p = member_slot(a.S, 0, m, L);
       GroupBias<true> gb;
-      if (tid < GK) gb.load(a.h + (size_t)uniform(L.mem[0]) * a.I * 2, tid);
+      if (tid < GK) gb.load(a.h + (size_t)p * a.I * 2, tid);
       uint4 wq[GW];
       ScalePack<P> sc[GW / P];
       const uint8_t* qb = a.dn_q + (size_t)e * a.dn_q_stride + ((size_t)(b * GK + g0) * kWave + lane) * 16;
@@ -344,22 +451,23 @@ __global__ __launch_bounds__(kBlock) void k_down(const ExpArgs a) {
       const uint16_t* sb = a.dn_s + (size_t)e * a.dn_s_stride + ((size_t)(b * (GK / P) + g0 / P) * kWave + lane) * P;
 #pragma unroll
       for (int j = 0; j < GW / P; ++j) sc[j].load(sb + (size_t)j * kWave * P);
-      for (int c = 0; c < nmem; ++c) {
-        const int p = uniform(L.mem[c]);
+      for (int c = 0; c < U.nmem; ++c) {
+        if (c > 0) {
+          p = member_slot(a.S, c, m, L);
+          if (tid < GK) gb.load(a.h + (size_t)p * a.I * 2, tid);
+        }
         const uint16_t* act = a.h + (size_t)p * a.I * 2;
-        if (c > 0 && tid < GK) gb.load(act, tid);
         if (tid < GK) L.bias[tid] = gb.value();
-        __syncthreads();
-        const float acc = active ? routed_dot<GW, P, true>(wq, sc, act, L.bias, g0, magic) : 0.f;
-        L.red[wave][lane] = acc;
-        __syncthreads();
+        lds_sync();
+        L.red[wave][lane] = active ? routed_dot<GW, P, true>(wq, sc, act, L.bias, g0, magic) : 0.f;
+        lds_sync();
         if (tid < kWave) {
           float part = 0.f;
 #pragma unroll
           for (int w = 0; w < kWavesPerBlock; ++w) part += L.red[w][tid];
-          a.dpart[(size_t)p * a.H + 64 * b + tid] = part;
+          st_coherent(&a.dpart[(size_t)p * a.H + 64 * b + tid], part);
         }
-        __syncthreads();
+        lds_sync();
       }
     }
   } else if constexpr (CW == 0) {
@@ -376,14 +484,14 @@ __global__ __launch_bounds__(kBlock) void k_down(const ExpArgs a) {
     for (int c = 0; c < CW; ++c) wc[c] = *reinterpret_cast<const uint4*>(base + (size_t)c * kWave * 16);
     for (int t = 0; t < a.M; ++t) {
       L.red[wave][lane] = shared_dot<CW, true>(wc, a.h_sh + (size_t)t * a.I * 2, c0);
-      __syncthreads();
+      lds_sync();
       if (tid < kWave) {
         float part = 0.f;
 #pragma unroll
         for (int w = 0; w < kWavesPerBlock; ++w) part += L.red[w][tid];
-        a.shdn_part[((size_t)t * a.KSdn + ks) * a.H + 64 * b + tid] = part;
+        st_coherent(&a.shdn_part[((size_t)t * a.KSdn + ks) * a.H + 64 * b + tid], part);
       }
-      __syncthreads();
+      lds_sync();
     }
   }
   if (!arrive_last(&a.dn_cnt[b], expected, &L.flag)) return;

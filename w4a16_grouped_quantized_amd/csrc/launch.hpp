@@ -13,6 +13,7 @@ constexpr int kMaxExperts = 512;   // LDS tables are sized for this
 constexpr int kMaxSlots = 4096;    // M * k handled by the decode (GEMV) kernels
 constexpr int kMaxTopK = 64;
 constexpr int kMaxGroups = 128;    // K/32 of the largest K (LDS group table)
+constexpr int kMaxKSplit = 8;      // K slices of a shared-expert tile across workgroups
 
 struct Shape {
   int H, E, k, I, has_shared;

@@ -59,7 +59,7 @@ __host__ __device__
 inline SharedSplit shared_split_for(int K, int target_chunks_per_wave) {
   SharedSplit s{1, K / 8 / kWavesPerBlock};
   // largest KS with K/8/4 divisible by KS and chunks per wave >= target
-  for (int ks = 1; ks <= 16; ++ks) {
+  for (int ks = 1; ks <= 8; ++ks) {
     int chunks = K / 8 / kWavesPerBlock;
     if (chunks % ks) continue;
     if (chunks / ks < target_chunks_per_wave) break;

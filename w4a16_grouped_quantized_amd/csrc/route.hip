@@ -35,46 +35,119 @@ __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// Top-k of logits[0..E) for one token, by one wavefront.  E <= 512: lane l
-// holds experts l + 64*j.
-__device__ void topk_token(const RouteArgs& a, int t, int lane) {
+// k-th largest of one 32-bit key per lane (keys of absent lanes are 0),
+// found bit by bit from the top with one ballot per bit.
+__device__ __forceinline__ uint32_t kth_largest_lane_key(uint32_t key, int k) {
+  uint32_t thr = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    if (__popcll(__ballot(key >= cand)) >= k) thr = cand;
+  }
+  return thr;
+}
+
+// Top-k of logits[0..E) for one token, by one wavefront (E <= 512: lane l
+// holds experts l + 64*j as order-preserving keys).
+//  1. Prune: the k-th largest of the 64 lane maxima is at most the k-th
+//     largest logit (those k maxima are k distinct logits), so only logits
+//     at or above it can win; typically about k of them survive.
+//  2. If more than 64 survive (heavy ties), select exactly instead: the k-th
+//     largest key bit by bit over all keys, every key above it, and the
+//     lowest ids among the keys equal to it.
+//  3. The survivors are gathered into lanes 0..C-1 and ranked by
+//     (key desc, id asc); ranks 0..k-1 are the result, in that order.
+__device__ void topk_token(const RouteArgs& a, int t, int lane, int* lds) {
   constexpr int EPL = kMaxExperts / kWave;
   uint32_t key[EPL];
-  uint32_t avail = 0;
+  bool present[EPL];
+  float val[EPL];
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
     const int e = lane + kWave * j;
-    key[j] = 0;
-    if (e < a.E) {
-      key[j] = sort_key(a.logits[(size_t)t * a.E + e]);
-      avail |= 1u << j;
-    }
+    present[j] = e < a.E;
+    val[j] = present[j] ? ld_coherent(&a.logits[(size_t)t * a.E + e]) : 0.f;
   }
-  uint32_t sel_key = 0;
-  int sel_id = 0;
-  for (int r = 0; r < a.k; ++r) {
-    uint32_t bk = 0;
-    int bi = 0x7FFFFFFF;
+  uint32_t lmax = 0;
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) {
-      // ascending j means ascending id inside a lane: strict > keeps the lower id
-      if (((avail >> j) & 1u) && (bi == 0x7FFFFFFF || key[j] > bk)) { bk = key[j]; bi = lane + kWave * j; }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const uint32_t ok = __shfl_xor(bk, off, 64);
-      const int oi = __shfl_xor(bi, off, 64);
-      if (ok > bk || (ok == bk && oi < bi)) { bk = ok; bi = oi; }
-    }
-    if ((bi & (kWave - 1)) == lane) avail &= ~(1u << (bi / kWave));
-    if (lane == r) { sel_key = bk; sel_id = bi; }
+  for (int j = 0; j < EPL; ++j) {
+    key[j] = present[j] ? sort_key(val[j]) : 0u;  // real keys of finite logits are > 0
+    lmax = key[j] > lmax ? key[j] : lmax;
   }
-  const float v = lane < a.k ? key_value(sel_key) : 0.f;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const uint32_t thr0 = kth_largest_lane_key(lmax, a.k);
+  uint32_t cand = 0;
+  int C = 0;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const bool c = present[j] && key[j] >= thr0;
+    cand |= (uint32_t)c << j;
+    C += __popcll(__ballot(c));
+  }
+  if (C > kWave) {
+    // exact selection of exactly k entries
+    uint32_t thr = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cb = thr | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) cnt += __popcll(__ballot(present[j] && key[j] >= cb));
+      if (cnt >= a.k) thr = cb;
+    }
+    int room = a.k;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) room -= __popcll(__ballot(present[j] && key[j] > thr));
+    cand = 0;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {  // ascending j, then lane: ascending id
+      const bool eq = present[j] && key[j] == thr;
+      const uint64_t eb = __ballot(eq);
+      const bool take = (present[j] && key[j] > thr) || (eq && __popcll(eb & lt) < room);
+      cand |= (uint32_t)take << j;
+      room -= __popcll(eb);
+      if (room < 0) room = 0;
+    }
+    C = a.k;
+  }
+  // gather the C candidates into lanes 0..C-1 (through LDS)
+  uint32_t* lkey = reinterpret_cast<uint32_t*>(lds);
+  int* lid = lds + kWave;
+  int* lorder = lds + 2 * kWave;
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const bool c = (cand >> j) & 1u;
+    const uint64_t bal = __ballot(c);
+    if (c) {
+      const int pos = base + __popcll(bal & lt);
+      lkey[pos] = key[j];
+      lid[pos] = lane + kWave * j;
+    }
+    base += __popcll(bal);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  const uint32_t mk = lane < C ? lkey[lane] : 0u;
+  const int mi = lane < C ? lid[lane] : 0x7FFFFFFF;
+  int rank = 0;
+  for (int c = 0; c < C; ++c) {
+    const uint32_t ok = (uint32_t)__builtin_amdgcn_readlane((int)mk, c);
+    const int oi = __builtin_amdgcn_readlane(mi, c);
+    rank += (ok > mk || (ok == mk && oi < mi)) ? 1 : 0;
+  }
+  if (lane < C && rank < a.k) lorder[rank] = lane;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  const int src = lane < a.k ? lorder[lane] : 0;
+  const uint32_t rk = __shfl(mk, src, 64);
+  const int ri = __shfl(mi, src, 64);
+  const float v = lane < a.k ? key_value(rk) : 0.f;
   const float vmax = __shfl(v, 0, 64);
   const float ex = lane < a.k ? expf(v - vmax) : 0.f;
   const float sum = wave_sum(ex);
   if (lane < a.k) {
-    a.ids[(size_t)t * a.k + lane] = sel_id;
+    a.ids[(size_t)t * a.k + lane] = ri;
     a.w[(size_t)t * a.k + lane] = ex / sum;
   }
 }
@@ -82,6 +155,7 @@ __device__ void topk_token(const RouteArgs& a, int t, int lane) {
 template <int NI>
 __global__ __launch_bounds__(kBlock) void k_route(const RouteArgs a) {
   __shared__ int flag;
+  __shared__ int topk_lds[kWavesPerBlock][3 * kMaxTopK];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int e = blockIdx.x * kWavesPerBlock + wave;
   const bool has_row = e < a.E;
@@ -134,10 +208,10 @@ __global__ __launch_bounds__(kBlock) void k_route(const RouteArgs a) {
       acc = fmaf(wr[i].w, xv[i][3], acc);
     }
     acc = wave_sum(acc);
-    if (has_row && lane == 0) a.logits[(size_t)t * a.E + e] = acc;
+    if (has_row && lane == 0) st_coherent(&a.logits[(size_t)t * a.E + e], acc);
   }
   if (!arrive_last(a.cnt, gridDim.x, &flag)) return;
-  for (int t = wave; t < a.M; t += kWavesPerBlock) topk_token(a, t, lane);
+  for (int t = wave; t < a.M; t += kWavesPerBlock) topk_token(a, t, lane, topk_lds[wave]);
 }
 
 namespace {
