@@ -15,6 +15,8 @@ Other workloads (for measurement runs; the default is the one reported):
   --workload verify2 / verify4   M = 2 / 4 tokens per step (speculative verify)
   --workload stack               one token through 40 stacked layers with
                                  RMSNorm between them (one step = 40 layers)
+  --workload prefill             one chunk of M = 4096 tokens per step (router
+                                 GEMM, grouped expert GEMMs on the matrix cores)
 
 Prints one JSON line.
 """
@@ -53,8 +55,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=4096)
     p.add_argument("--warmup", type=int, default=512)
-    p.add_argument("--workload", default="decode", choices=["decode", "verify2", "verify4", "stack"])
-    p.add_argument("--copies", type=int, default=32, help="resident layer copies to rotate over")
+    p.add_argument("--workload", default="decode", choices=["decode", "verify2", "verify4", "stack", "prefill"])
+    p.add_argument("--copies", type=int, default=None,
+                   help="resident layer copies to rotate over (default 32; 1 for prefill, which reads every expert)")
     p.add_argument("--chunk", type=int, default=256, help="steps captured per graph")
     p.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -85,7 +88,12 @@ def main():
     B.lib()
     shape = synth.LING
     cfg = B.config(shape)
-    M = {"decode": 1, "verify2": 2, "verify4": 4, "stack": 1}[args.workload]
+    M = {"decode": 1, "verify2": 2, "verify4": 4, "stack": 1, "prefill": 4096}[args.workload]
+    prefill = args.workload == "prefill"
+    if args.copies is None:
+        args.copies = 1 if prefill else 32
+    if prefill:
+        args.chunk = min(args.chunk, 4)
     n_layers = 40 if args.workload == "stack" else args.copies
 
     t0 = time.time()
@@ -170,34 +178,70 @@ def main():
     log(f"{steps} steps in {ms:.2f} ms (wall {wall * 1e3:.2f} ms): {ms_per_step * 1e3:.2f} us/step, "
         f"{gbs:.0f} GB/s, unique experts/step {uniq:.2f}")
 
-    # Per-stage kernel durations, eager, HIP events on the launch stream around
-    # each single-kernel call (route, gate_up, down) for the same rotation.
-    def time_stages(n):
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n)]
-        for i in range(n):
-            pk, rt = copies[i % n_layers]
-            j = i % chunk
-            x_in = X[j * M:(j + 1) * M]
-            e = ev[i]
-            e[0].record(stream)
-            B.route(cfg, rt, x_in, ids[j], w[j], ws.buf)
-            e[1].record(stream)
-            e[2].record(stream)
-            B.gate_up(cfg, pk, x_in, ids[j], ws.buf)
-            e[3].record(stream)
-            e[4].record(stream)
-            B.down(cfg, pk, ids[j], w[j], out[j], ws.buf)
-            e[5].record(stream)
-        torch.cuda.synchronize()
-        r = np.array([[e[2 * s].elapsed_time(e[2 * s + 1]) for s in range(3)] for e in ev]) * 1e3
-        return np.median(r, axis=0), np.mean(r, axis=0)
+    if prefill:
+        # route (router GEMM + top-k) and forward (permutation, grouped GEMMs,
+        # combine) timed separately, eager, HIP events on the launch stream
+        def time_calls(n):
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+            for i in range(n):
+                pk, rt = copies[i % n_layers]
+                j = i % chunk
+                x_in = X[j * M:(j + 1) * M]
+                e = ev[i]
+                e[0].record(stream)
+                B.route(cfg, rt, x_in, ids[j], w[j], ws.buf)
+                e[1].record(stream)
+                B.forward(cfg, pk, x_in, ids[j], w[j], out[j], ws.buf)
+                e[2].record(stream)
+            torch.cuda.synchronize()
+            r = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])] for e in ev]) * 1e3
+            return np.median(r, axis=0), np.mean(r, axis=0)
 
-    time_stages(min(32, args.stage_steps))
-    st_med, st_mean = time_stages(args.stage_steps)
-    log(f"stage us (median) route {st_med[0]:.2f} gate_up {st_med[1]:.2f} down {st_med[2]:.2f}; "
-        f"(mean) {st_mean[0]:.2f} {st_mean[1]:.2f} {st_mean[2]:.2f}")
-    gu_bytes = (uniq if args.workload != "stack" else 8) * EXPERT_GU_BYTES + SHARED_GU_BYTES + M * 2560 * 2
-    achieved = gu_bytes / (st_mean[1] * 1e-6) / 1e9
+        time_calls(2)
+        st_med, st_mean = time_calls(max(4, min(args.stage_steps, 16)))
+        log(f"call us (median) route {st_med[0]:.1f} forward {st_med[1]:.1f}; (mean) {st_mean[0]:.1f} {st_mean[1]:.1f}")
+        pairs = M * shape.top_k
+        flops = 2.0 * pairs * (2 * 768 * 2560 + 2560 * 768) + 2.0 * M * (2 * 768 * 2560 + 2560 * 768)
+        tflops = flops / (st_mean[1] * 1e-6) / 1e12
+        stage = {"route": round(float(st_mean[0]), 3), "forward": round(float(st_mean[1]), 3)}
+        roof = {"bound": "mfma", "kernel": "moe_forward_w4a16 at M=4096 (grouped GEMM kernels + permutation + combine)",
+                "achieved": round(tflops, 2), "peak": 2500.0, "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4),
+                "traffic": None, "flops_per_launch": flops}
+    else:
+        # Per-stage kernel durations, eager, HIP events on the launch stream
+        # around each single-kernel call (route, gate_up, down) for the same
+        # rotation.
+        def time_stages(n):
+            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n)]
+            for i in range(n):
+                pk, rt = copies[i % n_layers]
+                j = i % chunk
+                x_in = X[j * M:(j + 1) * M]
+                e = ev[i]
+                e[0].record(stream)
+                B.route(cfg, rt, x_in, ids[j], w[j], ws.buf)
+                e[1].record(stream)
+                e[2].record(stream)
+                B.gate_up(cfg, pk, x_in, ids[j], ws.buf)
+                e[3].record(stream)
+                e[4].record(stream)
+                B.down(cfg, pk, ids[j], w[j], out[j], ws.buf)
+                e[5].record(stream)
+            torch.cuda.synchronize()
+            r = np.array([[e[2 * s].elapsed_time(e[2 * s + 1]) for s in range(3)] for e in ev]) * 1e3
+            return np.median(r, axis=0), np.mean(r, axis=0)
+
+        time_stages(min(32, args.stage_steps))
+        st_med, st_mean = time_stages(args.stage_steps)
+        log(f"stage us (median) route {st_med[0]:.2f} gate_up {st_med[1]:.2f} down {st_med[2]:.2f}; "
+            f"(mean) {st_mean[0]:.2f} {st_mean[1]:.2f} {st_mean[2]:.2f}")
+        gu_bytes = (uniq if args.workload != "stack" else 8) * EXPERT_GU_BYTES + SHARED_GU_BYTES + M * 2560 * 2
+        achieved = gu_bytes / (st_mean[1] * 1e-6) / 1e9
+        stage = {"route": round(float(st_mean[0]), 3), "gate_up": round(float(st_mean[1]), 3),
+                 "down_combine": round(float(st_mean[2]), 3)}
+        roof = {"bound": "hbm", "kernel": "k_gate_up (routed int4 gate_up + SiLU, shared bf16 gate_up)",
+                "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "bytes_per_launch": int(gu_bytes)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -221,18 +265,15 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": {"decode": "ling_moe_layer_decode_m1", "verify2": "ling_moe_layer_verify_m2",
-                         "verify4": "ling_moe_layer_verify_m4", "stack": "ling_moe_stack40_decode_m1"}[args.workload],
+                         "verify4": "ling_moe_layer_verify_m4", "stack": "ling_moe_stack40_decode_m1",
+                         "prefill": "ling_moe_layer_prefill_m4096"}[args.workload],
             "hidden": 2560, "n_experts": 512, "top_k": 8, "moe_intermediate": 768, "group_size": 32,
             "tokens_per_step": M, "resident_layer_copies": n_layers, "graph_steps_per_replay": chunk,
             "algorithmic_bytes_per_step": int(bytes_per_step), "unique_experts_per_step": uniq,
             "compute": dtype,
         },
-        "stage_us": {"route": round(float(st_mean[0]), 3), "gate_up": round(float(st_mean[1]), 3),
-                     "down_combine": round(float(st_mean[2]), 3)},
-        "roofline": {"bound": "hbm", "kernel": "k_gate_up (routed int4 gate_up + SiLU, shared bf16 gate_up)",
-                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                     "bytes_per_launch": int(gu_bytes)},
+        "stage_us": stage,
+        "roofline": roof,
         "cpu_baseline": cpu,
         "build": B.build_info(),
     }

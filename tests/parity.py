@@ -8,8 +8,9 @@ Parity rules (readings of the pages where they leave the comparison open):
   the set is checked only up to that band.
 - routing weights: within 1e-5 of the softmax over the GPU's ids computed
   from the oracle's fp64 logits.
-- outputs: max |gpu - oracle| <= 2e-2 * rms(oracle output of the call), with
-  the oracle fed the GPU's ids and the fp64 weights for them.
+- outputs: max |gpu - oracle| <= 2e-2 * rms(oracle output of the call) plus
+  the rounding of the bf16 output itself (half a bf16 ulp of the oracle
+  value), with the oracle fed the GPU's ids and the fp64 weights for them.
 """
 from __future__ import annotations
 
@@ -63,12 +64,29 @@ def check_ids(shape, ids_gpu, w_gpu, ids_o, gap, logits_o):
     return w_ref
 
 
+def bf16_half_ulp(v: np.ndarray) -> np.ndarray:
+    """Half a bf16 unit in the last place of each value (8 significant bits):
+    the largest error of rounding v to bf16 to nearest."""
+    _, ex = np.frexp(np.abs(v))            # |v| = m * 2^ex, m in [0.5, 1)
+    return np.where(v == 0, 0.0, np.ldexp(1.0, ex - 9))
+
+
 def check_out(out_gpu_bits, out_ref, what=""):
+    """max |gpu - oracle| <= 2e-2 * rms(oracle), read as a bound on the
+    computation: the layer output is a bf16 tensor, and its one rounding to
+    bf16 (up to half a bf16 ulp of the value, which alone passes 2e-2 * rms
+    wherever |out| > 5.1 * rms) is allowed on top.  Returns the plain ratio
+    max|err| / rms."""
     got = bf16_f64(out_gpu_bits)
     rms = float(np.sqrt(np.mean(out_ref ** 2)))
-    err = float(np.max(np.abs(got - out_ref)))
+    diff = np.abs(got - out_ref)
+    err = float(np.max(diff))
+    excess = float(np.max(diff - bf16_half_ulp(out_ref)))
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
-    assert err <= OUT_TOL * rms, f"{what}: max|err| {err:.4g} > {OUT_TOL} * rms {rms:.4g} (ratio {err / rms:.3g})"
+    assert excess <= OUT_TOL * rms, (
+        f"{what}: max(|err| - half bf16 ulp) {excess:.4g} > {OUT_TOL} * rms {rms:.4g} "
+        f"(plain max|err|/rms {err / rms:.3g})")
+    check_out.last_excess = excess / rms
     return err / rms
 
 
@@ -115,4 +133,6 @@ def run_and_check(dl: DeviceLayer, oracle, x_bits: np.ndarray, what: str = ""):
     w_ref = check_ids(dl.shape, ids_g, w_g, ids_o, gap, logits_o)
     out_ref, bad = oracle.forward(dl.shape, dl.layer, x_bits, ids_g, w_ref)
     assert bad == 0
-    return check_out(from_dev_bf16(out), out_ref, what)
+    ratio = check_out(from_dev_bf16(out), out_ref, what)
+    print(f"{what}: max|err|/rms {ratio:.3e}, beyond the bf16 store {check_out.last_excess:.3e}", flush=True)
+    return ratio

@@ -50,10 +50,11 @@ def _cfg(**kw):
 
 def test_sizes(lib):
     c = B.config(synth.LING)
-    # packed blob = plain bytes (routed codes + scales + shared), each section 256-aligned
+    # packed blob = plain bytes (routed codes + scales + shared) + 16 bytes of
+    # range data per expert, each section 256-aligned
     E, H, I = 512, 2560, 768
     plain = E * (2 * I * H // 2 + 2 * I * (H // 32) * 2 + H * I // 2 + H * (I // 32) * 2) + (2 * I * H + H * I) * 2
-    assert B.packed_size(c) == plain
+    assert B.packed_size(c) == plain + E * 16
     assert B.workspace_size(c, 1) > 0
     assert B.workspace_size(c, 4) > B.workspace_size(c, 1)
     assert B.packed_size(_cfg(group_size=64)) == 0
@@ -100,8 +101,10 @@ def test_pointer_and_size_validation(lib):
     assert lib.moe_forward_w4a16(ctypes.byref(c), a, a, 1, a, a, None, a, big, None) == -1
     assert lib.moe_forward_w4a16(ctypes.byref(c), odd, a, 1, a, a, a, a, big, None) == -3
     assert lib.moe_forward_w4a16(ctypes.byref(c), a, a, 1, a, a, a, a, 64, None) == -4
-    # more slots than the decode kernels take
-    assert lib.moe_forward_w4a16(ctypes.byref(c), a, a, 1 << 12, a, a, a, a, big, None) == -5
+    # more (token, slot) pairs than the small-M kernels take, for a shape the
+    # many-token kernels are not compiled for (the tiny layer)
+    tiny = B.config(synth.TINY)
+    assert lib.moe_forward_w4a16(ctypes.byref(tiny), a, a, 2049, a, a, a, a, big, None) == -5
     assert lib.moe_permute(ctypes.byref(c), a, 4, None, a, a, a, big, None) == -1
     assert lib.moe_permute(ctypes.byref(c), a, 4, a, a, a, a, 8, None) == -4
     w = B.MoeWeightsPlain(a, a, a, a, None, None)   # shared expert missing while has_shared = 1

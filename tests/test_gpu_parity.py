@@ -35,9 +35,19 @@ def tiny():
 
 
 @pytest.fixture(scope="module")
-def ling():
+def ling_layer():
     _say("generating Ling-shape layer (seed 1)")
-    return DeviceLayer(synth.make_layer(synth.LING, 1), max_tokens=64)
+    return synth.make_layer(synth.LING, 1)
+
+
+@pytest.fixture(scope="module")
+def ling(ling_layer):
+    return DeviceLayer(ling_layer, max_tokens=64)
+
+
+@pytest.fixture(scope="module")
+def ling_big(ling_layer):
+    return DeviceLayer(ling_layer, max_tokens=4096)
 
 
 # ------------------------------------------------------------------ tiny layer
@@ -134,9 +144,9 @@ def test_permute_bit_exact(oracle_mod):
     from w4a16_grouped_quantized_amd import binding as B
     shape = synth.LING
     cfg = B.config(shape)
-    ws = B.Workspace(cfg, 1)
+    ws = B.Workspace(cfg, 4096)
     rng = np.random.default_rng(1)
-    for M in (1, 4, 257, 4096):
+    for M in (1, 4, 257, 300, 4096):
         ids = rng.integers(0, shape.n_experts, size=(M, shape.top_k)).astype(np.int32)
         if M > 4:
             ids[3, 1] = -7
@@ -213,3 +223,42 @@ def test_m0_is_noop(ling):
     out = ling.forward(x, ids, w)
     torch.cuda.synchronize()
     assert out.shape == (0, synth.LING.hidden)
+
+
+# ------------------------------------------------------------------ many tokens (prefill)
+
+@pytest.mark.parametrize("M", [40, 100, 600])
+def test_ling_many_tokens_full_check(ling_big, oracle_mod, M):
+    # 40: router as MFMA GEMM, experts on the small-M kernels; 100 and 600:
+    # both on the matrix cores (grouped GEMMs with ragged 64-row tiles)
+    _say(f"ling M={M}")
+    x = synth.make_tokens(synth.LING, 300 + M, M)
+    ratio = run_and_check(ling_big, oracle_mod, x, f"ling M={M}")
+    _say(f"ling M={M}: max|err|/rms = {ratio:.3e}")
+
+
+def test_ling_prefill_chunk_4096_sampled(ling_big, oracle_mod):
+    import torch
+    shape = synth.LING
+    M = 4096
+    x = synth.make_tokens(shape, 3, M)
+    x_dev = to_dev_bf16(x)
+    ids, w = ling_big.route(x_dev)
+    out = ling_big.forward(x_dev, ids, w)
+    out2 = ling_big.forward(x_dev, ids, w)
+    torch.cuda.synchronize()
+    assert ling_big.device_error() == 0
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), "prefill forward not deterministic"
+    ids_g, w_g, out_g = ids.cpu().numpy(), w.cpu().numpy(), from_dev_bf16(out)
+    rng = np.random.default_rng(4096)
+    rows = np.sort(rng.choice(M, size=48, replace=False))
+    ids_o, _, gap, logits_o = oracle_mod.route(shape, ling_big.layer.router_w, x[rows])
+    w_ref = check_ids(shape, ids_g[rows], w_g[rows], ids_o, gap, logits_o)
+    out_ref, bad = oracle_mod.forward(shape, ling_big.layer, x[rows], ids_g[rows], w_ref)
+    assert bad == 0
+    ratio = check_out(out_g[rows], out_ref, "prefill 4096 sampled rows")
+    # every row: finite, and the routing of all 4096 rows is a valid top-k
+    assert np.all(np.isfinite(bf16_f64(out_g)))
+    assert np.all((ids_g >= 0) & (ids_g < shape.n_experts))
+    assert np.all(np.abs(w_g.sum(1) - 1) < 1e-5)
+    _say(f"prefill 4096: sampled 48 rows, max|err|/rms = {ratio:.3e}")

@@ -312,3 +312,16 @@ def test_rmsnorm_worked_values(oracle_mod):
     # four equal entries: the result is 1 / sqrt(1 + 1e-6), i.e. 1.0 in bf16
     y4 = synth.bf16_bits(np.ones((1, 4)))
     np.testing.assert_array_equal(oracle_mod.rmsnorm(y4, 1e-6), [[0x3F80] * 4])
+
+
+def test_parity_rounding_allowance_is_half_bf16_ulp(oracle_mod):
+    # the output check allows the bf16 store of the result on top of the
+    # tolerance; that allowance must be exactly the worst rounding error
+    from parity import bf16_half_ulp
+    rng = np.random.default_rng(12)
+    v = rng.standard_normal(200000) * np.exp(rng.uniform(-20, 20, 200000))
+    r = synth.bf16_bits_to_f32(oracle_mod.f64_to_bf16(v)).astype(np.float64)
+    q = np.abs(r - v) / bf16_half_ulp(v)
+    assert q.max() <= 1.0 and q.max() > 0.999
+    # values on a binade edge: 1 has half-ulp 2^-8, just below 1 it is 2^-9
+    assert bf16_half_ulp(np.array([1.0, 0.999, -3.0, 0.0])).tolist() == [2.0 ** -8, 2.0 ** -9, 2.0 ** -7, 0.0]

@@ -13,6 +13,14 @@ using namespace moe;
 namespace {
 
 constexpr float kRmsEps = 1e-6f;
+// Token counts at which the many-token path takes over (when a kernel is
+// compiled for the shape): the router as an MFMA GEMM beyond 32 tokens, the
+// experts as grouped MFMA GEMMs beyond 512 (token, slot) pairs.
+constexpr int kRouteGemmMinTokens = 33;
+constexpr int64_t kPrefillMinSlots = 513;
+
+bool route_gemm(const Shape& s, int M) { return M >= kRouteGemmMinTokens && prefill_supported(s); }
+bool experts_gemm(const Shape& s, int M) { return (int64_t)M * s.k >= kPrefillMinSlots && prefill_supported(s); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -62,7 +70,13 @@ int moe_pack_weights(const moe_config* cfg, const moe_weights_plain* src, void* 
 size_t moe_workspace_size(const moe_config* cfg, int32_t max_tokens) {
   Shape s;
   if (check_cfg(cfg, &s) != MOE_OK || max_tokens < 0) return 0;
-  return ws_layout(s.H, s.E, s.k, s.I, s.has_shared, max_tokens < 1 ? 1 : max_tokens).total;
+  const int M = max_tokens < 1 ? 1 : max_tokens;
+  size_t n = ws_layout(s.H, s.E, s.k, s.I, s.has_shared, M).total;
+  if (prefill_supported(s)) {
+    const size_t p = pf_layout(s.H, s.E, s.k, s.I, s.has_shared, M).total;
+    n = p > n ? p : n;
+  }
+  return n;
 }
 
 int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
@@ -83,6 +97,12 @@ int moe_route(const moe_config* cfg, const float* router_w, const uint16_t* x, i
   if (!aligned16(router_w) || !aligned16(x) || !aligned16(ws) || !aligned4(topk_ids) || !aligned4(topk_w) ||
       (rms && !aligned16(x_norm)))
     return MOE_ERR_ALIGN;
+  if (route_gemm(s, M) && !rms) {
+    const PfLayout P = pf_layout(s.H, s.E, s.k, s.I, s.has_shared, M);
+    if (ws_bytes < P.total) return MOE_ERR_WORKSPACE;
+    return launched(launch_prefill_route(s, router_w, x, M, topk_ids, topk_w, static_cast<uint8_t*>(ws), P,
+                                         static_cast<hipStream_t>(stream)));
+  }
   if (!route_supported(s)) return MOE_ERR_UNSUPPORTED;
   const WsLayout L = ws_layout(s.H, s.E, s.k, s.I, s.has_shared, M);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
@@ -139,6 +159,20 @@ int moe_forward_w4a16(const moe_config* cfg, const void* packed, const uint16_t*
                       void* stream) {
   Shape s;
   WsLayout L;
+  {
+    int rc0 = check_cfg(cfg, &s);
+    if (rc0 == MOE_OK && M > 0 && experts_gemm(s, M)) {
+      if (!packed || !x || !topk_ids || !topk_w || !out || !ws) return MOE_ERR_NULL;
+      if (!aligned16(packed) || !aligned16(x) || !aligned16(out) || !aligned16(ws) || !aligned4(topk_ids) ||
+          !aligned4(topk_w))
+        return MOE_ERR_ALIGN;
+      const PfLayout P = pf_layout(s.H, s.E, s.k, s.I, s.has_shared, M);
+      if (ws_bytes < P.total) return MOE_ERR_WORKSPACE;
+      const PackedLayout PL = packed_layout(s.H, s.E, s.I, s.has_shared);
+      return launched(launch_prefill_forward(s, static_cast<const uint8_t*>(packed), PL, x, M, topk_ids, topk_w, out,
+                                             static_cast<uint8_t*>(ws), P, static_cast<hipStream_t>(stream)));
+    }
+  }
   int rc = check_experts(cfg, &s, packed, x, M, topk_ids, topk_w, out, ws, ws_bytes, true, true, &L);
   if (rc != MOE_OK || M == 0) return rc;
   const PackedLayout P = packed_layout(s.H, s.E, s.I, s.has_shared);
@@ -159,11 +193,11 @@ int moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t M, int32
   if (!counts || !offsets || !ws || (M > 0 && (!topk_ids || !perm))) return MOE_ERR_NULL;
   if (!aligned4(counts) || !aligned4(offsets) || !aligned4(perm) || !aligned4(topk_ids) || !aligned16(ws))
     return MOE_ERR_ALIGN;
-  const WsLayout L = ws_layout(s.H, s.E, s.k, s.I, s.has_shared, 1);
+  const WsLayout L = ws_layout(s.H, s.E, s.k, s.I, s.has_shared, M < 1 ? 1 : M);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
-  return launched(launch_permute(s, topk_ids, M, counts, offsets, perm,
-                                 reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + L.err),
-                                 static_cast<hipStream_t>(stream)));
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  return launched(launch_permute(s, topk_ids, M, counts, offsets, perm, reinterpret_cast<int32_t*>(w8 + L.ghist),
+                                 reinterpret_cast<int32_t*>(w8 + L.err), static_cast<hipStream_t>(stream)));
 }
 
 int moe_get_device_error(void* ws, void* stream, int32_t* code_host) {
@@ -197,11 +231,12 @@ const char* moe_status_string(int status) {
 }
 
 const char* moe_build_info(void) {
-  return "arch=gfx950 layout=tile64-lanerow-v1 "
-         "route=wave-per-row-fp32+lastwg-topk "
+  return "arch=gfx950 layout=tile64-lanerow-v2 "
+         "route=wave-per-row-fp32+lastwg-topk|mfma-bf16x3(M>=33) "
          "gate_up=int4-dot2bf16-sgpr-act(GW20P4|GW2P2)+shared-bf16(KS-split,lastwg) "
          "down=int4-dot2bf16(GW6P2|GW1P1)+lastwg-combine "
-         "permute=1wg-stable-counting-sort "
+         "prefill(M*k>=513)=grouped-mfma-f16-exact-int4(128-row items,xcd-aware)+shared-mfma-bf16 "
+         "permute=multi-wg-stable-counting-sort "
          "max_experts=512 max_decode_slots=4096";
 }
 

@@ -18,6 +18,7 @@ struct WsLayout {
   size_t shgu_part;                          // fp32 [Mmax][Tgu][KSgu][64]
   size_t dpart;                              // fp32 [Mmax*k][H]
   size_t shdn_part;                          // fp32 [Mmax][KSdn][H]
+  size_t ghist;                              // int32 [perm_groups(Mmax*k)][E] (moe_permute)
   size_t total;
   int Tgu, Tdn, KSgu, KSdn, CWgu, CWdn;
 };
@@ -27,6 +28,24 @@ struct WsLayout {
 inline SharedSplit shared_gu_split(int H) { return shared_split_for(H, ksplit_for(H / kGroup).GW); }
 inline SharedSplit shared_dn_split(int I) { return shared_split_for(I, ksplit_for(I / kGroup).GW); }
 
+// Stable grouping of the (token, slot) pairs by expert runs in workgroups of
+// kPermSeg pairs; per-workgroup expert histograms live in the workspace.
+constexpr int kPermSeg = 2048;
+inline int perm_groups(long long S) { return (int)((S + kPermSeg - 1) / kPermSeg); }
+
+// Both paths share one header: the error word at offset 0 and the decode
+// path's arrival counters, which must stay zero between calls whichever path
+// ran last.  Per-call arrays follow the header.
+inline size_t ws_header(int H, int I, size_t* err, size_t* route_cnt, size_t* shgu_cnt, size_t* dn_cnt) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+  *err = take(4);
+  *route_cnt = take(4);
+  *shgu_cnt = take((size_t)4 * (I / 32));
+  *dn_cnt = take((size_t)4 * (H / 64));
+  return off;
+}
+
 inline WsLayout ws_layout(int H, int E, int k, int I, int has_shared, int Mmax) {
   WsLayout w;
   w.Tgu = I / 32;
@@ -35,12 +54,8 @@ inline WsLayout ws_layout(int H, int E, int k, int I, int has_shared, int Mmax) 
   SharedSplit sd = shared_dn_split(I);
   w.KSgu = sg.KS; w.CWgu = sg.CW;
   w.KSdn = sd.KS; w.CWdn = sd.CW;
-  size_t off = 0;
+  size_t off = ws_header(H, I, &w.err, &w.route_cnt, &w.shgu_cnt, &w.dn_cnt);
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
-  w.err = take(4);
-  w.route_cnt = take(4);
-  w.shgu_cnt = take((size_t)4 * w.Tgu);
-  w.dn_cnt = take((size_t)4 * w.Tdn);
   size_t M = (size_t)Mmax;
   w.logits = take(M * E * 4);
   w.h = take(M * k * I * 2 * 2);                  // (hi, lo) per value
@@ -48,6 +63,53 @@ inline WsLayout ws_layout(int H, int E, int k, int I, int has_shared, int Mmax) 
   w.shgu_part = take(has_shared ? M * w.Tgu * w.KSgu * 64 * 4 : 0);
   w.dpart = take(M * k * H * 4);
   w.shdn_part = take(has_shared ? M * w.KSdn * H * 4 : 0);
+  w.ghist = take((size_t)perm_groups((long long)M * k) * E * 4);  // moe_permute
+  w.total = off;
+  return w;
+}
+
+// Rows of one work item of the grouped GEMMs (an expert's sorted rows are cut
+// into items of at most this many: three 32-row MFMA blocks).
+constexpr int kItemRows = 96;
+
+// Workspace of the many-token (prefill) path.
+struct PfLayout {
+  size_t err, route_cnt, shgu_cnt, dn_cnt;
+  size_t logits;                    // fp32 [M][E]
+  size_t counts, offsets;           // int32 [E], [E+1]
+  size_t perm, inv;                 // int32 [S]: pair at each sorted position, sorted position of each pair
+  size_t ghist;                     // int32 [perm_groups(S)][E]
+  size_t tile_e, tile_j, ntile;     // int32 [items], [items], [1]: work items (expert, row block)
+  size_t xh, rexp;                  // fp16 [M][H] scaled rows of x, int32 [M] their exponents
+  size_t hbuf;                      // fp16 [S][I] scaled h per sorted position
+  size_t hsh;                       // bf16 [2][M][I] shared-expert h as (hi, lo) planes
+  size_t y, ysh;                    // fp32 [S][H] per sorted position, [M][H]
+  size_t total;
+  int items;                        // bound on the routed work items
+};
+
+inline PfLayout pf_layout(int H, int E, int k, int I, int has_shared, int M) {
+  PfLayout w;
+  size_t off = ws_header(H, I, &w.err, &w.route_cnt, &w.shgu_cnt, &w.dn_cnt);
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+  const size_t S = (size_t)M * k;
+  // sum over experts of ceil(count / kItemRows) <= E + S / kItemRows
+  w.items = E + (int)((S + kItemRows - 1) / kItemRows);
+  w.logits = take((size_t)M * E * 4);
+  w.counts = take((size_t)E * 4);
+  w.offsets = take((size_t)(E + 1) * 4);
+  w.perm = take(S * 4);
+  w.inv = take(S * 4);
+  w.ghist = take((size_t)perm_groups((long long)S) * E * 4);
+  w.tile_e = take((size_t)w.items * 4);
+  w.tile_j = take((size_t)w.items * 4);
+  w.ntile = take(4);
+  w.xh = take((size_t)M * H * 2);
+  w.rexp = take((size_t)M * 4);
+  w.hbuf = take(S * I * 2);
+  w.hsh = take(has_shared ? (size_t)2 * M * I * 2 : 0);
+  w.y = take(S * H * 4);
+  w.ysh = take(has_shared ? (size_t)M * H * 4 : 0);
   w.total = off;
   return w;
 }

@@ -35,8 +35,24 @@ hipError_t launch_down(const Shape& s, const uint8_t* packed, const PackedLayout
                        const int32_t* ids, const float* w, uint16_t* out, uint8_t* ws, const WsLayout& L,
                        hipStream_t st);
 
-hipError_t launch_permute(const Shape& s, const int32_t* ids, int M, int32_t* counts,
-                          int32_t* offsets, int32_t* perm, int32_t* err, hipStream_t st);
+hipError_t launch_permute(const Shape& s, const int32_t* ids, int M, int32_t* counts, int32_t* offsets,
+                          int32_t* perm, int32_t* ghist, int32_t* err, hipStream_t st);
+
+// The permutation plus its inverse (sorted position of each pair) and the
+// work items of the grouped GEMMs: item i < *ntile covers rows
+// [kItemRows * tile_j[i], ...) of expert tile_e[i]'s sorted run.
+hipError_t launch_permute_items(const Shape& s, const int32_t* ids, int M, int32_t* counts, int32_t* offsets,
+                                int32_t* perm, int32_t* inv, int32_t* tile_e, int32_t* tile_j, int32_t* ntile,
+                                int32_t* ghist, int32_t* err, hipStream_t st);
+
+// Many-token path (prefill): router GEMM + per-token top-k, and the grouped
+// expert GEMMs on the matrix cores.
+bool prefill_supported(const Shape& s);
+hipError_t launch_prefill_route(const Shape& s, const float* router_w, const uint16_t* x, int M, int32_t* ids,
+                                float* w, uint8_t* ws, const PfLayout& P, hipStream_t st);
+hipError_t launch_prefill_forward(const Shape& s, const uint8_t* packed, const PackedLayout& PL, const uint16_t* x,
+                                  int M, const int32_t* ids, const float* w, uint16_t* out, uint8_t* ws,
+                                  const PfLayout& P, hipStream_t st);
 
 hipError_t launch_pack(const Shape& s, const uint8_t* w13_q, const uint16_t* w13_s,
                        const uint8_t* w2_q, const uint16_t* w2_s, const uint16_t* sh_w13,

@@ -18,6 +18,11 @@
 // Shared BF16 matrices: tile b, chunk c of 8 inputs, lane l:
 //   16 bytes at ((tile * K/8 + c) * 64 + lane) * 16, inputs in natural order;
 //   same row-to-lane mapping as the routed matrices.
+// Per-expert range data (kMetaWords uint32 per expert, float bit patterns of
+// non-negative values, used by the many-token kernels to scale fp16 operands
+// by powers of two):
+//   [0] max |scale| of gate_up, [1] max |scale| of down,
+//   [2] max over r < I of ||gate row r||_1 * ||up row r||_1 (dequantised).
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -69,9 +74,11 @@ inline SharedSplit shared_split_for(int K, int target_chunks_per_wave) {
   return s;
 }
 
+constexpr int kMetaWords = 4;
+
 struct PackedLayout {
   // byte offsets of each section inside the packed buffer
-  size_t gu_q, gu_s, dn_q, dn_s, sh_gu, sh_dn, total;
+  size_t gu_q, gu_s, dn_q, dn_s, sh_gu, sh_dn, meta, total;
   // per-expert strides in bytes
   size_t gu_q_stride, gu_s_stride, dn_q_stride, dn_s_stride;
 };
@@ -94,6 +101,7 @@ inline PackedLayout packed_layout(int H, int E, int I, int has_shared) {
   L.dn_s = off; off = (off + L.dn_s_stride * E + 255) / 256 * 256;
   L.sh_gu = off; if (has_shared) off = (off + (size_t)2 * I * H * 2 + 255) / 256 * 256;
   L.sh_dn = off; if (has_shared) off = (off + (size_t)H * I * 2 + 255) / 256 * 256;
+  L.meta = off; off = (off + (size_t)E * kMetaWords * 4 + 255) / 256 * 256;
   L.total = off;
   return L;
 }

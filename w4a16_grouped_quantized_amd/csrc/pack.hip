@@ -69,6 +69,61 @@ __global__ void k_pack_bf16(const uint16_t* __restrict__ src, uint16_t* __restri
   }
 }
 
+// Range data of each expert (layout.hpp): non-negative floats combined
+// with an integer atomic max on their bit patterns, which orders them like
+// the values and makes the result independent of the order of arrival.
+__device__ __forceinline__ void max_bits(uint32_t* p, float v) {
+  atomicMax(reinterpret_cast<unsigned int*>(p), __float_as_uint(v));
+}
+
+// One wavefront per gate row r (and its up row I + r) of one expert: the
+// dequantised L1 norms of both rows (lane l takes groups l, l + 64, ...),
+// their product into word 2, and the largest |scale| into word 0.
+__global__ __launch_bounds__(256) void k_pack_meta_gu(const uint8_t* __restrict__ q, const uint16_t* __restrict__ sc,
+                                                      uint32_t* __restrict__ meta, int H, int I) {
+  const int e = blockIdx.y;
+  const int r = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= I) return;
+  const int GK = H / kGroup;
+  float norm[2] = {0.f, 0.f}, smax = 0.f;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const size_t row = (size_t)e * 2 * I + (size_t)(half ? I + r : r);
+    for (int g = lane; g < GK; g += kWave) {
+      const uint4 w = *reinterpret_cast<const uint4*>(q + row * (H / 2) + (size_t)g * 16);
+      const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+      int sum = 0;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int n = 0; n < 8; ++n) sum += abs((int)((wd[d] >> (4 * n)) & 0xFu) - 8);
+      const float s = fabsf(bf16_to_f32(sc[row * GK + g]));
+      norm[half] += s * (float)sum;
+      smax = fmaxf(smax, s);
+    }
+  }
+  const float prod = wave_sum(norm[0]) * wave_sum(norm[1]);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) smax = fmaxf(smax, __shfl_xor(smax, off, 64));
+  if (lane == 0) {
+    max_bits(meta + (size_t)e * kMetaWords + 0, smax);
+    max_bits(meta + (size_t)e * kMetaWords + 2, prod);
+  }
+}
+
+// Largest |scale| of each expert's down matrix into word 1.
+__global__ __launch_bounds__(256) void k_pack_meta_dn(const uint16_t* __restrict__ sc, uint32_t* __restrict__ meta,
+                                                      size_t per_e) {
+  const int e = blockIdx.y;
+  float m = 0.f;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < per_e; i += (size_t)gridDim.x * blockDim.x)
+    m = fmaxf(m, fabsf(bf16_to_f32(sc[(size_t)e * per_e + i])));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if ((threadIdx.x & 63) == 0) max_bits(meta + (size_t)e * kMetaWords + 1, m);
+}
+
 __global__ void k_fill_zero(uint4* __restrict__ p, size_t n16, uint8_t* __restrict__ tail, size_t ntail) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
     p[i] = make_uint4(0, 0, 0, 0);
@@ -104,6 +159,13 @@ hipError_t launch_pack(const Shape& s, const uint8_t* w13_q, const uint16_t* w13
   n = (size_t)E * (H / 64) * (I / kGroup / kd.P) * kWave;
   hipLaunchKernelGGL(k_pack_scales, dim3(grid_for(n)), dim3(256), 0, st, w2_s,
                      reinterpret_cast<uint16_t*>(packed + P.dn_s), E, H, I, 0, I, kd.P, P.dn_s_stride / 2);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  uint32_t* meta = reinterpret_cast<uint32_t*>(packed + P.meta);
+  if ((err = launch_fill_zero(meta, (size_t)E * kMetaWords * 4, st)) != hipSuccess) return err;
+  hipLaunchKernelGGL(k_pack_meta_gu, dim3((I + kWavesPerBlock - 1) / kWavesPerBlock, E), dim3(256), 0, st, w13_q,
+                     w13_s, meta, H, I);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(k_pack_meta_dn, dim3(8, E), dim3(256), 0, st, w2_s, meta, (size_t)H * (I / kGroup));
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (s.has_shared) {
     n = (size_t)(2 * I / 64) * (H / 8) * kWave;

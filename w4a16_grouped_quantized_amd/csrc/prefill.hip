@@ -1,0 +1,841 @@
+// prefill.hip — the many-token path (chunked prefill).  Every expert's
+// (token, slot) pairs form a dense block of rows, so the expert FFNs run as
+// grouped GEMMs on the matrix cores, fp32 accumulate throughout.
+//
+//   router:  logits[M][E] = x[M][H] * Wr^T   (Wr fp32 split exactly into three
+//            bf16 parts hi + mid + lo, one bf16 MFMA each; x is bf16)
+//   top-k:   one wavefront per token over its logits row
+//   permute: pairs grouped by expert (permute.hip), cut into work items of at
+//            most 128 rows
+//   x prep:  each token row of x scaled by a power of two 2^-r_t into fp16,
+//            largest magnitude below 2^15 (exact: bf16 has 8 significant bits,
+//            fp16 11)
+//   gate_up: per item, rows x[token] times the INT4 gate/up rows dequantised
+//            to fp16 as q * s * 2^p; h = silu(gate) * up, stored as fp16
+//            scaled by 2^-sigma with sigma from a bound on |h| (below)
+//   down:    h times the INT4 down rows, one fp32 row per sorted pair
+//   shared:  the same two GEMMs on all tokens with the BF16 shared weights in
+//            bf16 MFMAs (x as is, h as an exact-to-16-bits hi + lo pair)
+//   combine: out[t] = sum_j w[t][j] * y[pair (t, j)] + y_shared[t], slot order
+//
+// Exactness of the routed operands.  A code u (0..15, q = u - 8) becomes fp16
+// through the fp8 converter (a byte 0..15 read as e4m3 is u * 2^-9; the
+// converter's exponent scale 2^9 makes it u), then fma(u, s', -8 s') with
+// s' = s * 2^p in fp16: q * s' needs at most 3 + 8 significant bits, so the
+// fused result is exact in fp16's 11, and 2^p (per expert, from the largest
+// |scale|) keeps |q s'| <= 2^15.  The products of fp16 operands are exact in
+// the fp32 accumulators; the powers of two are taken out in the epilogues.
+// Bound on h: |g|, |u| <= max|x_t| * ||row||_1 and |silu(g)| <= |g|, so
+// |h| <= 2^(2 r_t + 30) * N_e with N_e = max_r ||gate_r||_1 ||up_r||_1
+// (computed when the weights are packed); sigma = 2 r_t + 16 + (exponent of
+// N_e) + 1 puts |h| 2^-sigma below 2^13, and h keeps fp16's 11 bits.
+#include <type_traits>
+
+#include "launch.hpp"
+
+namespace moe {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+// e with |v| < 2^e for finite v (0 and subnormals give -126).
+__device__ __forceinline__ int exp_above(float v) {
+  const int ex = (int)((__float_as_uint(v) >> 23) & 0xFFu);
+  return ex == 0 ? -126 : ex - 126;
+}
+
+// C[m][n] of a 32x32 MFMA block lives in lane n + 32*((m/4)%2), slot (m%4) + 4*(m/8).
+__device__ __forceinline__ int c_row(int lane, int slot) { return 8 * (slot >> 2) + 4 * (lane >> 5) + (slot & 3); }
+
+// Order of 8 consecutive K inputs inside a 16-byte fp16 operand of the INT4
+// GEMMs: position j holds input (j >> 1) + 4 (j & 1), the order in which the
+// converter produces the codes of one packed dword.  Input i sits at
+// position 2 (i & 3) + (i >> 2).
+__device__ __forceinline__ int k8_pos(int i) { return 2 * (i & 3) + (i >> 2); }
+
+// ------------------------------------------------------------------ x prep
+
+__global__ __launch_bounds__(kBlock) void k_pf_xprep(const uint16_t* __restrict__ x, int H,
+                                                     _Float16* __restrict__ xh, int32_t* __restrict__ rexp) {
+  __shared__ float red[kWavesPerBlock];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const uint4* row = reinterpret_cast<const uint4*>(x + (size_t)t * H);
+  const int nch = H / 8;
+  float m = 0.f;
+  for (int c = tid; c < nch; c += kBlock) {
+    const uint4 v = row[c];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      m = fmaxf(m, fabsf(bf16_to_f32(w[d] & 0xFFFFu)));
+      m = fmaxf(m, fabsf(bf16_to_f32(w[d] >> 16)));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const int r = exp_above(m) - 15;  // max |x| * 2^-r < 2^15
+  for (int c = tid; c < nch; c += kBlock) {
+    const uint4 v = row[c];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float f[8];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      f[2 * d] = ldexpf(bf16_to_f32(w[d] & 0xFFFFu), -r);
+      f[2 * d + 1] = ldexpf(bf16_to_f32(w[d] >> 16), -r);
+    }
+    f16x8_t o;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] = (_Float16)f[(j >> 1) + 4 * (j & 1)];
+    *reinterpret_cast<f16x8_t*>(xh + (size_t)t * H + 8 * c) = o;
+  }
+  if (tid == 0) rexp[t] = r;
+}
+
+// ------------------------------------------------------------------ grouped GEMMs
+
+enum GgKind { GG_RGU = 0, GG_RDN = 1, GG_SGU = 2, GG_SDN = 3 };
+
+constexpr int kGgKc = 128;             // K per LDS chunk (two 64-K steps)
+constexpr int kGgStride = kGgKc + 8;   // 16-bit elements per LDS row (16-byte pad: conflict-free MFMA reads)
+constexpr int kGgLdsRows = 128;
+
+struct GgArgs {
+  int M, E, k, H, I;
+  int K;        // reduction length
+  int ntiles;   // 64-row weight tiles (gate_up: I/32, down: H/64)
+  int ng;       // workgroups per item: ceil(ntiles / 4)
+  // routed work items (permute.hip)
+  const int32_t* __restrict__ counts;
+  const int32_t* __restrict__ offsets;
+  const int32_t* __restrict__ perm;
+  const int32_t* __restrict__ tile_e;
+  const int32_t* __restrict__ tile_j;
+  const int32_t* __restrict__ ntile;
+  // activations
+  const _Float16* __restrict__ xh;    // [M][H] scaled x, K order of k8_pos
+  const int32_t* __restrict__ rexp;   // [M]
+  const _Float16* __restrict__ hbuf;  // [S][I] scaled h per sorted position, K order of k8_pos
+  const uint16_t* __restrict__ x;     // [M][H] bf16
+  const uint16_t* __restrict__ hsh;   // [2][M][I] bf16 (hi, lo)
+  // weights of this phase
+  const uint8_t* __restrict__ q;      // routed packed codes
+  const uint16_t* __restrict__ s;     // routed packed scales
+  size_t q_stride, s_stride;          // per expert: bytes, elements
+  int P, pshift;                      // scales per lane-load of the packed layout (1, 2 or 4), log2 P
+  const uint16_t* __restrict__ shw;   // shared packed bf16
+  const uint32_t* __restrict__ meta;  // per-expert range data
+  int meta_word;                      // 0: gate_up scales, 1: down scales
+  // outputs
+  _Float16* __restrict__ hout;        // [S][I]
+  uint16_t* __restrict__ hsh_out;     // [2][M][I]
+  float* __restrict__ y;              // [S][H]
+  float* __restrict__ ysh;            // [M][H]
+};
+
+template <int KIND>
+struct GgCfg {
+  static constexpr bool ROUTED = KIND == GG_RGU || KIND == GG_RDN;
+  static constexpr bool HILO = KIND == GG_SDN;  // A is the shared h as hi + lo
+  static constexpr int MAXMB = ROUTED ? kItemRows / 32 : 2;  // 32-row MFMA blocks per item
+  static constexpr int ROWS = 32 * MAXMB;
+  static constexpr int DEPTH = ROUTED ? 4 : 2;  // 64-K steps of weights in flight
+};
+
+struct RawQ {  // one 64-K step of a routed weight tile: one 32-code group per lane half
+  uint4 c[2];
+  uint32_t s[2];
+};
+struct RawS {  // one 64-K step of a shared weight tile: four 8-input chunks per lane half
+  uint4 c[2][4];
+};
+
+__device__ __forceinline__ uint32_t dword_of(const uint4& v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+// Everything a workgroup knows about its item once the row tables are built.
+struct GgItem {
+  int e, base, nrow, p;
+};
+
+// Main loop and epilogue for items of NMB 32-row blocks.  The loop body has
+// no branches around memory operations (padding rows load row 0, prefetches
+// past the end reload the last step, the chunk store and barrier run
+// unconditionally), so the compiler can count the loads in flight and wait
+// only for the one each step consumes.
+template <int KIND, int NMB>
+__device__ __forceinline__ void gg_run(const GgArgs& a, const GgItem& it, uint16_t (*sA)[kGgLdsRows * kGgStride],
+                                       const int* sSrc, const int* sExp, const int* sSig) {
+  using C = GgCfg<KIND>;
+  using Raw = typename std::conditional<C::ROUTED, RawQ, RawS>::type;
+  const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
+  const int n = lane & 31, h = lane >> 5;
+  // ---- A chunks: thread covers 16-byte segment tid & 15 of rows (tid >> 4) + 16 jj
+  constexpr int NJ = C::HILO ? 8 : 2 * NMB;  // row groups of 16 that hold data
+  const int seg = tid & 15;
+  // byte offsets (all operands are far below 4 GiB) from a uniform base, so
+  // loads take the SGPR-base + 32-bit VGPR-offset form
+  const uint8_t* abase8;
+  if constexpr (C::HILO) abase8 = reinterpret_cast<const uint8_t*>(a.hsh);
+  else if constexpr (KIND == GG_RGU) abase8 = reinterpret_cast<const uint8_t*>(a.xh);
+  else if constexpr (KIND == GG_RDN) abase8 = reinterpret_cast<const uint8_t*>(a.hbuf);
+  else abase8 = reinterpret_cast<const uint8_t*>(a.x);
+  const uint32_t rowbytes = 2u * (KIND == GG_RGU || KIND == GG_SGU ? a.H : a.I);
+  uint32_t aoff[NJ];
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) {
+    const int R = (tid >> 4) + 16 * jj;
+    if constexpr (C::HILO)
+      aoff[jj] = (uint32_t)(R >> 6) * (uint32_t)a.M * rowbytes + (uint32_t)sSrc[R & 63] * rowbytes;
+    else
+      aoff[jj] = (uint32_t)sSrc[R] * rowbytes;
+    aoff[jj] += seg * 16;
+  }
+  // staging registers: one named value per row group (an indexed array here
+  // ends up in scratch memory)
+  uint4 st_0, st_1, st_2, st_3, st_4, st_5, st_6, st_7;
+  auto slot = [&](auto J) -> uint4& {
+    constexpr int j = decltype(J)::value;
+    if constexpr (j == 0) return st_0;
+    else if constexpr (j == 1) return st_1;
+    else if constexpr (j == 2) return st_2;
+    else if constexpr (j == 3) return st_3;
+    else if constexpr (j == 4) return st_4;
+    else if constexpr (j == 5) return st_5;
+    else if constexpr (j == 6) return st_6;
+    else return st_7;
+  };
+  auto for_each_jj = [&](auto f) {
+    auto one = [&](auto J) {
+      constexpr int j = decltype(J)::value;
+      if constexpr (j < NJ && (!C::HILO || (j & 3) < 2 * NMB)) f(J);
+    };
+    one(std::integral_constant<int, 0>{}); one(std::integral_constant<int, 1>{});
+    one(std::integral_constant<int, 2>{}); one(std::integral_constant<int, 3>{});
+    one(std::integral_constant<int, 4>{}); one(std::integral_constant<int, 5>{});
+    one(std::integral_constant<int, 6>{}); one(std::integral_constant<int, 7>{});
+  };
+  auto load_A = [&](int kc0) {
+    const uint8_t* ab = abase8 + 2 * kc0;
+    for_each_jj([&](auto J) { slot(J) = *reinterpret_cast<const uint4*>(ab + aoff[decltype(J)::value]); });
+  };
+  auto store_A = [&](int buf) {
+    for_each_jj([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      *reinterpret_cast<uint4*>(&sA[buf][((tid >> 4) + 16 * j) * kGgStride + seg * 8]) = slot(J);
+    });
+  };
+  // ---- this wavefront's weight tile (tiles past the last read tile 0 and are dropped)
+  const int t = (int)(blockIdx.x >> 3) % a.ng * kWavesPerBlock + wave;
+  const bool tile_ok = t < a.ntiles;
+  const int tt = tile_ok ? t : 0;
+  const int GK = a.K / kGroup;
+  const uint8_t* qe = a.q + (size_t)it.e * a.q_stride;
+  const uint16_t* se = a.s + (size_t)it.e * a.s_stride;
+  const uint8_t* sw = reinterpret_cast<const uint8_t*>(a.shw);
+  // per-lane parts of the weight offsets; the per-step parts are uniform
+  uint32_t boff[2], soff[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int row = 32 * nb + n;
+    if constexpr (C::ROUTED) {
+      boff[nb] = ((uint32_t)(tt * GK + h) * kWave + row) * 16;
+      // group g = 2 st + h: with P >= 2 the pack index g / P and slot g % P
+      // get h only in the slot; with P = 1 h is a whole pack (64 lanes) on
+      soff[nb] = ((uint32_t)tt * (GK >> a.pshift) * kWave + row) * a.P + (a.P >= 2 ? h : kWave * h);
+    } else {
+      boff[nb] = ((uint32_t)(tt * (a.K / 8) + h) * kWave + row) * 16;
+      soff[nb] = 0;
+    }
+  }
+  auto load_B = [&](int st, Raw& r) {
+    if constexpr (C::ROUTED) {
+      const uint8_t* qs = qe + (size_t)st * (2 * kWave * 16);
+      const int g0 = 2 * st;
+      const uint16_t* ss = se + (size_t)((g0 >> a.pshift) * kWave * a.P + (g0 & (a.P - 1)));
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        r.c[nb] = *reinterpret_cast<const uint4*>(qs + boff[nb]);
+        r.s[nb] = ss[soff[nb]];
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {  // 8-input chunk 8st + 2i + h
+          const uint8_t* ws = sw + (size_t)(8 * st + 2 * i) * (kWave * 16);
+          r.c[nb][i] = *reinterpret_cast<const uint4*>(ws + boff[nb]);
+        }
+    }
+  };
+  f32x16_t acc[NMB][2];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+  const float pscale = ldexpf(1.0f, it.p);
+  auto compute = [&](const Raw& r, int buf, int kk) {
+    if constexpr (C::ROUTED) {
+      f16x2_t s2[2], m2[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const _Float16 sh = (_Float16)(bf16_to_f32(r.s[nb]) * pscale);
+        s2[nb] = (f16x2_t){sh, sh};
+        m2[nb] = s2[nb] * (f16x2_t){(_Float16)-8.0f, (_Float16)-8.0f};
+      }
+      // sub-step i: lane half h takes dword i (inputs 8i..8i+7) of group 2st + h
+      const uint16_t* abase = &sA[buf][n * kGgStride + kk + 32 * h];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f16x8_t B[2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const uint32_t w = dword_of(r.c[nb], i);
+          const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+          f16x2_t c0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false);  // inputs 0, 4
+          f16x2_t c1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, true);   // inputs 1, 5
+          f16x2_t c2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, false);  // inputs 2, 6
+          f16x2_t c3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, true);   // inputs 3, 7
+          c0 = __builtin_elementwise_fma(c0, s2[nb], m2[nb]);
+          c1 = __builtin_elementwise_fma(c1, s2[nb], m2[nb]);
+          c2 = __builtin_elementwise_fma(c2, s2[nb], m2[nb]);
+          c3 = __builtin_elementwise_fma(c3, s2[nb], m2[nb]);
+          B[nb] = (f16x8_t){c0[0], c0[1], c1[0], c1[1], c2[0], c2[1], c3[0], c3[1]};
+        }
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          const f16x8_t A = *reinterpret_cast<const f16x8_t*>(abase + 32 * mb * kGgStride + 8 * i);
+          acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B[0], acc[mb][0], 0, 0, 0);
+          acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B[1], acc[mb][1], 0, 0, 0);
+        }
+      }
+    } else {
+      // sub-step i: lane half h takes inputs 16i + 8h .. +7 (natural order)
+      const uint16_t* abase = &sA[buf][n * kGgStride + kk + 8 * h];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8_t B0 = __builtin_bit_cast(bf16x8_t, r.c[0][i]);
+        const bf16x8_t B1 = __builtin_bit_cast(bf16x8_t, r.c[1][i]);
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(abase + 32 * mb * kGgStride + 16 * i);
+          acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B0, acc[mb][0], 0, 0, 0);
+          acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B1, acc[mb][1], 0, 0, 0);
+          if constexpr (C::HILO) {
+            const bf16x8_t A2 = *reinterpret_cast<const bf16x8_t*>(abase + (64 + 32 * mb) * kGgStride + 16 * i);
+            acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A2, B0, acc[mb][0], 0, 0, 0);
+            acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A2, B1, acc[mb][1], 0, 0, 0);
+          }
+        }
+      }
+    }
+  };
+  // ---- main loop: 64-K steps, weights DEPTH - 1 steps ahead in registers,
+  // activations one 128-K chunk ahead in registers, double-buffered in LDS
+  const int nsteps = a.K / 64;  // a multiple of 4
+  const int nch = nsteps / 2;
+  Raw ring[C::DEPTH];
+#pragma unroll
+  for (int d = 0; d < C::DEPTH - 1; ++d) load_B(d, ring[d]);
+  load_A(0);
+  store_A(0);
+  lds_sync();
+  load_A(kGgKc);
+  for (int st0 = 0; st0 < nsteps; st0 += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int st = st0 + u;
+      load_B(min(st + C::DEPTH - 1, nsteps - 1), ring[(u + C::DEPTH - 1) % C::DEPTH]);
+      compute(ring[u % C::DEPTH], (u >> 1) & 1, 64 * (u & 1));
+      if (u & 1) {
+        // end of chunk ch = st / 2: chunk ch + 1 into the other buffer (its last
+        // readers, chunk ch - 1, all passed the previous barrier)
+        const int ch = st >> 1;
+        store_A(((u >> 1) + 1) & 1);
+        lds_sync();
+        load_A(min(ch + 2, nch - 1) * kGgKc);
+      }
+    }
+  }
+  if (!tile_ok) return;
+  // ---- epilogue
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+    for (int sl = 0; sl < 16; ++sl) {
+      const int r = 32 * mb + c_row(lane, sl);
+      if (r >= it.nrow) continue;
+      if constexpr (KIND == GG_RGU) {
+        const int ex = sExp[r] - it.p;
+        const float g = ldexpf(acc[mb][0][sl], ex), u = ldexpf(acc[mb][1][sl], ex);
+        const float hv = ldexpf(silu_f32(g) * u, -sSig[r]);
+        const int col = 32 * t + n;
+        a.hout[(size_t)(it.base + r) * a.I + (col & ~7) + k8_pos(col & 7)] = (_Float16)hv;
+      } else if constexpr (KIND == GG_RDN) {
+        const int ex = sExp[r] - it.p;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          a.y[(size_t)(it.base + r) * a.H + 64 * t + 32 * nb + n] = ldexpf(acc[mb][nb][sl], ex);
+      } else if constexpr (KIND == GG_SGU) {
+        const float hv = silu_f32(acc[mb][0][sl]) * acc[mb][1][sl];
+        const uint16_t hi = f32_to_bf16(hv), lo = f32_to_bf16(hv - bf16_to_f32(hi));
+        const size_t o = (size_t)(it.base + r) * a.I + 32 * t + n;
+        a.hsh_out[o] = hi;
+        a.hsh_out[(size_t)a.M * a.I + o] = lo;
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          a.ysh[(size_t)(it.base + r) * a.H + 64 * t + 32 * nb + n] = acc[mb][nb][sl];
+      }
+    }
+  }
+}
+
+// One workgroup = one work item (up to 96 sorted rows of one expert, or a
+// block of tokens for the shared expert) x 4 weight tiles of 64 rows, one per
+// wavefront.  Workgroup ids are laid out so that the ng workgroups of one item
+// run back to back on one XCD (ids are dealt to the 8 XCDs round-robin), so
+// the item's activation rows are read from that XCD's L2 after the first.
+template <int KIND>
+__global__ __launch_bounds__(kBlock, 2) void k_gg(const GgArgs a) {
+  using C = GgCfg<KIND>;
+  __shared__ __align__(16) uint16_t sA[2][kGgLdsRows * kGgStride];
+  __shared__ int sSrc[C::ROWS];
+  __shared__ int sExp[C::ROWS];
+  __shared__ int sSig[C::ROWS];
+  const int tid = threadIdx.x;
+  // ---- work item
+  const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
+  const int item = (slot / a.ng) * 8 + xcd;
+  GgItem it{0, 0, 0, 0};
+  if constexpr (C::ROUTED) {
+    if (item >= uniform(a.ntile[0])) return;
+    it.e = uniform(a.tile_e[item]);
+    const int j = uniform(a.tile_j[item]);
+    it.base = uniform(a.offsets[it.e]) + kItemRows * j;
+    it.nrow = min(kItemRows, uniform(a.counts[it.e]) - kItemRows * j);
+  } else {
+    it.base = C::ROWS * item;
+    if (it.base >= a.M) return;
+    it.nrow = min(C::ROWS, a.M - it.base);
+  }
+  int ne = 0;
+  if constexpr (C::ROUTED) {
+    const uint32_t* mt = a.meta + (size_t)it.e * kMetaWords;
+    it.p = min(12 - exp_above(__uint_as_float(mt[a.meta_word])), 126);
+    ne = exp_above(__uint_as_float(mt[2])) + 1;
+  }
+  // ---- row tables: A source row and the exponents of each row
+  if (tid < C::ROWS) {
+    const int rr = tid < it.nrow ? tid : 0;  // padding rows repeat row 0; their results are dropped
+    if constexpr (KIND == GG_RGU) {
+      const int tok = a.perm[it.base + rr] / a.k;
+      const int r = a.rexp[tok];
+      sSrc[tid] = tok;
+      sExp[tid] = r;
+      sSig[tid] = 2 * r + 16 + ne;
+    } else if constexpr (KIND == GG_RDN) {
+      const int tok = a.perm[it.base + rr] / a.k;
+      sSrc[tid] = it.base + rr;
+      sExp[tid] = 2 * a.rexp[tok] + 16 + ne;
+    } else {
+      sSrc[tid] = it.base + rr;
+    }
+  }
+  lds_sync();
+  const int nmb = (it.nrow + 31) >> 5;
+  static_assert(C::MAXMB == 2 || C::MAXMB == 3, "item sizes handled below");
+  if constexpr (C::MAXMB == 3) {
+    if (nmb == 1) gg_run<KIND, 1>(a, it, sA, sSrc, sExp, sSig);
+    else if (nmb == 2) gg_run<KIND, 2>(a, it, sA, sSrc, sExp, sSig);
+    else gg_run<KIND, 3>(a, it, sA, sSrc, sExp, sSig);
+  } else {
+    if (nmb == 1) gg_run<KIND, 1>(a, it, sA, sSrc, sExp, sSig);
+    else gg_run<KIND, 2>(a, it, sA, sSrc, sExp, sSig);
+  }
+}
+
+// ------------------------------------------------------------------ router GEMM
+
+constexpr int kRtRows = 64;          // tokens per workgroup tile
+constexpr int kRtKc = 256;           // K per LDS chunk
+constexpr int kRtStride = kRtKc + 8;
+
+struct RtArgs {
+  int M, E, H;
+  const uint16_t* __restrict__ x;  // [M][H] bf16
+  const float* __restrict__ wr;    // [E][H] fp32
+  float* __restrict__ logits;      // [M][E]
+};
+
+// fp32 x 8 -> three bf16 x 8 parts with hi + mid + lo == v exactly.
+__device__ __forceinline__ void split3(const float (&v)[8], bf16x8_t& hi, bf16x8_t& mid, bf16x8_t& lo) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float hf = bf16_to_f32(f32_to_bf16(v[i]));
+    const float r = v[i] - hf;
+    const float mf = bf16_to_f32(f32_to_bf16(r));
+    hi[i] = __builtin_bit_cast(__bf16, f32_to_bf16(hf));
+    mid[i] = __builtin_bit_cast(__bf16, f32_to_bf16(mf));
+    lo[i] = __builtin_bit_cast(__bf16, f32_to_bf16(r - mf));
+  }
+}
+
+// Workgroup tile: 64 tokens x 256 experts (4 wavefronts x 64 router rows, as
+// two 32x32 MFMA blocks); x staged in LDS by chunks of 256 inputs; router rows
+// read a step ahead into registers and split there.
+__global__ __launch_bounds__(kBlock) void k_rt_gemm(const RtArgs a) {
+  __shared__ __align__(16) uint16_t sA[kRtRows * kRtStride];
+  const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
+  const int j = blockIdx.x;
+  const int nvalid = min(kRtRows, a.M - kRtRows * j);
+  const int lrow = tid >> 2, lpart = tid & 3;  // 64 rows x 4 threads, 64 inputs each per chunk
+  const uint16_t* arow = a.x + (size_t)(kRtRows * j + (lrow < nvalid ? lrow : 0)) * a.H;
+  const int tile = blockIdx.y * kWavesPerBlock + wave;
+  const bool tile_ok = tile < a.E / 64;
+  const int tsafe = tile_ok ? tile : 0;
+  const int n = lane & 31, h = lane >> 5;
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+  const bool two_mb = nvalid > 32;
+  struct Raw {
+    uint4 v[2][8];
+  };
+  auto load_raw = [&](int kg, Raw& r) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const float* wp = a.wr + (size_t)(64 * tsafe + 32 * nb + n) * a.H + kg;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        r.v[nb][2 * i] = *reinterpret_cast<const uint4*>(wp + 16 * i + 8 * h);
+        r.v[nb][2 * i + 1] = *reinterpret_cast<const uint4*>(wp + 16 * i + 8 * h + 4);
+      }
+    }
+  };
+  uint4 stage[8];
+  auto load_chunk = [&](int kc0) {
+    const uint4* src = reinterpret_cast<const uint4*>(arow + kc0 + lpart * 64);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) stage[i] = src[i];
+  };
+  auto store_chunk = [&]() {
+    uint4* dst = reinterpret_cast<uint4*>(sA + lrow * kRtStride + lpart * 64);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dst[i] = stage[i];
+  };
+  const int nsteps = a.H / 64;
+  Raw cur, nxt;
+  load_chunk(0);
+  load_raw(0, cur);
+  for (int st = 0; st < nsteps; ++st) {
+    const int kg = st * 64;
+    const int kk = kg % kRtKc;
+    if (kk == 0) {  // new LDS chunk: wait for every wavefront to finish the previous one
+      if (st > 0) lds_sync();
+      store_chunk();
+      lds_sync();
+      if (kg + kRtKc < a.H) load_chunk(kg + kRtKc);
+    }
+    if (st + 1 < nsteps) load_raw(kg + 64, nxt);
+    if (tile_ok) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bf16x8_t B[2], B2[2], B3[2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const uint4 v0 = cur.v[nb][2 * i], v1 = cur.v[nb][2 * i + 1];
+          const float v[8] = {__uint_as_float(v0.x), __uint_as_float(v0.y), __uint_as_float(v0.z),
+                              __uint_as_float(v0.w), __uint_as_float(v1.x), __uint_as_float(v1.y),
+                              __uint_as_float(v1.z), __uint_as_float(v1.w)};
+          split3(v, B[nb], B2[nb], B3[nb]);
+        }
+        const int koff = 16 * i + 8 * h;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          if (mb == 1 && !two_mb) break;
+          const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(sA + (32 * mb + n) * kRtStride + kk + koff);
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B[nb], acc[mb][nb], 0, 0, 0);
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B2[nb], acc[mb][nb], 0, 0, 0);
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B3[nb], acc[mb][nb], 0, 0, 0);
+          }
+        }
+      }
+    }
+    cur = nxt;
+  }
+  if (!tile_ok) return;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int sl = 0; sl < 16; ++sl) {
+      const int r = 32 * mb + c_row(lane, sl);
+      if (r >= nvalid) continue;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        a.logits[(size_t)(kRtRows * j + r) * a.E + 64 * tile + 32 * nb + n] = acc[mb][nb][sl];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ top-k rows
+
+struct TopkArgs {
+  int M, E, k;
+  const float* __restrict__ logits;
+  int32_t* __restrict__ ids;
+  float* __restrict__ w;
+};
+
+__device__ __forceinline__ uint32_t pf_sort_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float pf_key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// One wavefront per token: the same selection rule as the decode router
+// (k largest logits, ties to the lower id, softmax over them), written for
+// logits that a previous launch produced.
+__global__ __launch_bounds__(kBlock) void k_topk_rows(const TopkArgs a) {
+  __shared__ int lds_all[kWavesPerBlock][3 * kWave];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * kWavesPerBlock + wave;
+  if (t >= a.M) return;
+  int* lds = lds_all[wave];
+  constexpr int EPL = kMaxExperts / kWave;
+  uint32_t key[EPL];
+  bool present[EPL];
+  uint32_t lmax = 0;
+#pragma unroll
+  for (int jj = 0; jj < EPL; ++jj) {
+    const int e = lane + kWave * jj;
+    present[jj] = e < a.E;
+    key[jj] = present[jj] ? pf_sort_key(a.logits[(size_t)t * a.E + e]) : 0u;
+    lmax = key[jj] > lmax ? key[jj] : lmax;
+  }
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // the k-th largest lane maximum bounds the k-th largest key from below
+  uint32_t thr0 = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cb = thr0 | (1u << bit);
+    if (__popcll(__ballot(lmax >= cb)) >= a.k) thr0 = cb;
+  }
+  uint32_t cand = 0;
+  int C = 0;
+#pragma unroll
+  for (int jj = 0; jj < EPL; ++jj) {
+    const bool c = present[jj] && key[jj] >= thr0;
+    cand |= (uint32_t)c << jj;
+    C += __popcll(__ballot(c));
+  }
+  if (C > kWave) {  // exact selection of the k-th key, ties to the lower id
+    uint32_t thr = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cb = thr | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int jj = 0; jj < EPL; ++jj) cnt += __popcll(__ballot(present[jj] && key[jj] >= cb));
+      if (cnt >= a.k) thr = cb;
+    }
+    int room = a.k;
+#pragma unroll
+    for (int jj = 0; jj < EPL; ++jj) room -= __popcll(__ballot(present[jj] && key[jj] > thr));
+    cand = 0;
+#pragma unroll
+    for (int jj = 0; jj < EPL; ++jj) {
+      const bool eq = present[jj] && key[jj] == thr;
+      const uint64_t eb = __ballot(eq);
+      const bool take = (present[jj] && key[jj] > thr) || (eq && __popcll(eb & lt) < room);
+      cand |= (uint32_t)take << jj;
+      room -= __popcll(eb);
+      if (room < 0) room = 0;
+    }
+    C = a.k;
+  }
+  uint32_t* lkey = reinterpret_cast<uint32_t*>(lds);
+  int* lid = lds + kWave;
+  int* lorder = lds + 2 * kWave;
+  int base = 0;
+#pragma unroll
+  for (int jj = 0; jj < EPL; ++jj) {
+    const bool c = (cand >> jj) & 1u;
+    const uint64_t bal = __ballot(c);
+    if (c) {
+      const int pos = base + __popcll(bal & lt);
+      lkey[pos] = key[jj];
+      lid[pos] = lane + kWave * jj;
+    }
+    base += __popcll(bal);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  const uint32_t mk = lane < C ? lkey[lane] : 0u;
+  const int mi = lane < C ? lid[lane] : 0x7FFFFFFF;
+  int rank = 0;
+  for (int c = 0; c < C; ++c) {
+    const uint32_t ok = (uint32_t)__builtin_amdgcn_readlane((int)mk, c);
+    const int oi = __builtin_amdgcn_readlane(mi, c);
+    rank += (ok > mk || (ok == mk && oi < mi)) ? 1 : 0;
+  }
+  if (lane < C && rank < a.k) lorder[rank] = lane;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  const int src = lane < a.k ? lorder[lane] : 0;
+  const uint32_t rk = __shfl(mk, src, 64);
+  const int ri = __shfl(mi, src, 64);
+  const float v = lane < a.k ? pf_key_value(rk) : 0.f;
+  const float vmax = __shfl(v, 0, 64);
+  const float ex = lane < a.k ? expf(v - vmax) : 0.f;
+  const float sum = wave_sum(ex);
+  if (lane < a.k) {
+    a.ids[(size_t)t * a.k + lane] = ri;
+    a.w[(size_t)t * a.k + lane] = ex / sum;
+  }
+}
+
+// ------------------------------------------------------------------ combine
+
+struct CombineArgs {
+  int M, E, k, H, has_shared;
+  const int32_t* __restrict__ ids;
+  const float* __restrict__ topk_w;
+  const int32_t* __restrict__ inv;  // sorted position of each pair
+  const float* __restrict__ y;      // [S][H] per sorted position
+  const float* __restrict__ ysh;    // [M][H]
+  uint16_t* __restrict__ out;
+  int32_t* __restrict__ err;
+};
+
+// One thread per 4 outputs of one token: the y rows of the token's k slots
+// are summed in slot order, then the shared expert's row.
+__global__ __launch_bounds__(kBlock) void k_pf_combine(const CombineArgs a) {
+  const size_t q = (size_t)blockIdx.x * kBlock + threadIdx.x;  // quad index
+  const size_t per_tok = a.H / 4;
+  if (q >= (size_t)a.M * per_tok) return;
+  const int t = (int)(q / per_tok);
+  const int n0 = (int)(q % per_tok) * 4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  bool bad = false;
+  for (int jj = 0; jj < a.k; ++jj) {
+    const int p = t * a.k + jj;
+    const int e = a.ids[p];
+    if (e < 0 || e >= a.E) { bad = true; continue; }
+    const float wv = a.topk_w[p];
+    const float4 v = *reinterpret_cast<const float4*>(a.y + (size_t)a.inv[p] * a.H + n0);
+    acc.x = fmaf(wv, v.x, acc.x); acc.y = fmaf(wv, v.y, acc.y);
+    acc.z = fmaf(wv, v.z, acc.z); acc.w = fmaf(wv, v.w, acc.w);
+  }
+  if (a.has_shared) {
+    const float4 v = *reinterpret_cast<const float4*>(a.ysh + (size_t)t * a.H + n0);
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  uint2 o;
+  o.x = (uint32_t)f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
+  o.y = (uint32_t)f32_to_bf16(acc.z) | ((uint32_t)f32_to_bf16(acc.w) << 16);
+  *reinterpret_cast<uint2*>(a.out + (size_t)t * a.H + n0) = o;
+  if (bad) atomicOr(a.err, 1);
+}
+
+// ------------------------------------------------------------------ host side
+
+bool prefill_supported(const Shape& s) {
+  // K of both GEMMs a whole number of 256-input blocks (four 64-K steps);
+  // weight tiles of 64 rows; router tiles of 64 experts
+  return s.H % 256 == 0 && s.I % 256 == 0 && s.E % 64 == 0;
+}
+
+static int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+hipError_t launch_prefill_route(const Shape& s, const float* router_w, const uint16_t* x, int M, int32_t* ids,
+                                float* w, uint8_t* ws, const PfLayout& P, hipStream_t st) {
+  RtArgs a{M, s.E, s.H, x, router_w, reinterpret_cast<float*>(ws + P.logits)};
+  hipLaunchKernelGGL(k_rt_gemm, dim3(ceil_div(M, kRtRows), ceil_div(s.E / 64, kWavesPerBlock)), dim3(kBlock), 0, st,
+                     a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  TopkArgs t{M, s.E, s.k, a.logits, ids, w};
+  hipLaunchKernelGGL(k_topk_rows, dim3(ceil_div(M, kWavesPerBlock)), dim3(kBlock), 0, st, t);
+  return hipGetLastError();
+}
+
+// Grid of a grouped GEMM: items rounded up to a multiple of the 8 XCDs, times
+// the workgroups per item.
+static dim3 gg_grid(int items, int ng) { return dim3((unsigned)(8 * ceil_div(items, 8) * ng)); }
+
+hipError_t launch_prefill_forward(const Shape& s, const uint8_t* packed, const PackedLayout& PL, const uint16_t* x,
+                                  int M, const int32_t* ids, const float* w, uint16_t* out, uint8_t* ws,
+                                  const PfLayout& P, hipStream_t st) {
+  auto i32 = [&](size_t off) { return reinterpret_cast<int32_t*>(ws + off); };
+  int32_t* err = i32(P.err);
+  hipError_t e = launch_permute_items(s, ids, M, i32(P.counts), i32(P.offsets), i32(P.perm), i32(P.inv),
+                                      i32(P.tile_e), i32(P.tile_j), i32(P.ntile), i32(P.ghist), err, st);
+  if (e != hipSuccess) return e;
+  _Float16* xh = reinterpret_cast<_Float16*>(ws + P.xh);
+  hipLaunchKernelGGL(k_pf_xprep, dim3(M), dim3(kBlock), 0, st, x, s.H, xh, i32(P.rexp));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const KSplit kg = ksplit_for(s.H / kGroup), kd = ksplit_for(s.I / kGroup);
+  GgArgs a{};
+  a.M = M; a.E = s.E; a.k = s.k; a.H = s.H; a.I = s.I;
+  a.counts = i32(P.counts); a.offsets = i32(P.offsets); a.perm = i32(P.perm);
+  a.tile_e = i32(P.tile_e); a.tile_j = i32(P.tile_j); a.ntile = i32(P.ntile);
+  a.xh = xh; a.rexp = i32(P.rexp);
+  a.hbuf = reinterpret_cast<const _Float16*>(ws + P.hbuf);
+  a.x = x;
+  a.hsh = reinterpret_cast<const uint16_t*>(ws + P.hsh);
+  a.meta = reinterpret_cast<const uint32_t*>(packed + PL.meta);
+  a.hout = reinterpret_cast<_Float16*>(ws + P.hbuf);
+  a.hsh_out = reinterpret_cast<uint16_t*>(ws + P.hsh);
+  a.y = reinterpret_cast<float*>(ws + P.y);
+  a.ysh = reinterpret_cast<float*>(ws + P.ysh);
+  // gate_up
+  a.K = s.H;
+  a.ntiles = s.I / 32;
+  a.ng = ceil_div(a.ntiles, kWavesPerBlock);
+  a.q = packed + PL.gu_q; a.s = reinterpret_cast<const uint16_t*>(packed + PL.gu_s);
+  a.q_stride = PL.gu_q_stride; a.s_stride = PL.gu_s_stride / 2; a.P = kg.P; a.pshift = kg.P == 4 ? 2 : kg.P - 1;
+  a.shw = reinterpret_cast<const uint16_t*>(packed + PL.sh_gu);
+  a.meta_word = 0;
+  hipLaunchKernelGGL(k_gg<GG_RGU>, gg_grid(P.items, a.ng), dim3(kBlock), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (s.has_shared) {
+    hipLaunchKernelGGL(k_gg<GG_SGU>, gg_grid(ceil_div(M, GgCfg<GG_SGU>::ROWS), a.ng), dim3(kBlock), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // down
+  a.K = s.I;
+  a.ntiles = s.H / 64;
+  a.ng = ceil_div(a.ntiles, kWavesPerBlock);
+  a.q = packed + PL.dn_q; a.s = reinterpret_cast<const uint16_t*>(packed + PL.dn_s);
+  a.q_stride = PL.dn_q_stride; a.s_stride = PL.dn_s_stride / 2; a.P = kd.P; a.pshift = kd.P == 4 ? 2 : kd.P - 1;
+  a.shw = reinterpret_cast<const uint16_t*>(packed + PL.sh_dn);
+  a.meta_word = 1;
+  hipLaunchKernelGGL(k_gg<GG_RDN>, gg_grid(P.items, a.ng), dim3(kBlock), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (s.has_shared) {
+    hipLaunchKernelGGL(k_gg<GG_SDN>, gg_grid(ceil_div(M, GgCfg<GG_SDN>::ROWS), a.ng), dim3(kBlock), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  CombineArgs c{M, s.E, s.k, s.H, s.has_shared, ids, w, i32(P.inv), a.y, a.ysh, out, err};
+  const size_t quads = (size_t)M * (s.H / 4);
+  hipLaunchKernelGGL(k_pf_combine, dim3((unsigned)((quads + kBlock - 1) / kBlock)), dim3(kBlock), 0, st, c);
+  return hipGetLastError();
+}
+
+}  // namespace moe
