@@ -46,6 +46,11 @@ ROUTER_BYTES = 512 * 2560 * 4                                           # 5,242,
 TOKEN_IO_BYTES = 2 * 2560 * 2                                           # x in, out back
 
 
+WORKLOAD_NAMES = {"decode": "ling_moe_layer_decode_m1", "verify2": "ling_moe_layer_verify_m2",
+                  "verify4": "ling_moe_layer_verify_m4", "stack": "ling_moe_stack40_decode_m1",
+                  "prefill": "ling_moe_layer_prefill_m4096"}
+
+
 def step_bytes(n_unique_experts: int, M: int) -> int:
     return n_unique_experts * EXPERT_BYTES + SHARED_GU_BYTES + SHARED_DN_BYTES + ROUTER_BYTES + M * TOKEN_IO_BYTES
 
@@ -62,6 +67,8 @@ def parse():
     p.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--stage-steps", type=int, default=256, help="eager steps timed per stage")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="after timing, run a plain device copy of this many MiB (reference for HBM byte counters)")
     return p.parse_args()
 
 
@@ -208,33 +215,47 @@ def main():
                 "achieved": round(tflops, 2), "peak": 2500.0, "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4),
                 "traffic": None, "flops_per_launch": flops}
     else:
-        # Per-stage kernel durations, eager, HIP events on the launch stream
-        # around each single-kernel call (route, gate_up, down) for the same
-        # rotation.
-        def time_stages(n):
-            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n)]
-            for i in range(n):
-                pk, rt = copies[i % n_layers]
-                j = i % chunk
-                x_in = X[j * M:(j + 1) * M]
-                e = ev[i]
-                e[0].record(stream)
-                B.route(cfg, rt, x_in, ids[j], w[j], ws.buf)
-                e[1].record(stream)
-                e[2].record(stream)
-                B.gate_up(cfg, pk, x_in, ids[j], ws.buf)
-                e[3].record(stream)
-                e[4].record(stream)
-                B.down(cfg, pk, ids[j], w[j], out[j], ws.buf)
-                e[5].record(stream)
-            torch.cuda.synchronize()
-            r = np.array([[e[2 * s].elapsed_time(e[2 * s + 1]) for s in range(3)] for e in ev]) * 1e3
-            return np.median(r, axis=0), np.mean(r, axis=0)
+        # Per-stage kernel durations: for each stage (route, gate_up, down) a
+        # graph of n back-to-back launches of that stage alone over the same
+        # rotation of layer copies, replayed between HIP events on the launch
+        # stream; duration per launch = elapsed / n.
+        def stage_graph(stage, n):
+            gs = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gs):
+                for i in range(n):
+                    pk, rt = copies[i % n_layers]
+                    j = i % chunk
+                    x_in = X[j * M:(j + 1) * M]
+                    if stage == 0:
+                        B.route(cfg, rt, x_in, ids[j], w[j], ws.buf)
+                    elif stage == 1:
+                        B.gate_up(cfg, pk, x_in, ids[j], ws.buf)
+                    else:
+                        B.down(cfg, pk, ids[j], w[j], out[j], ws.buf)
+            return gs
 
-        time_stages(min(32, args.stage_steps))
-        st_med, st_mean = time_stages(args.stage_steps)
-        log(f"stage us (median) route {st_med[0]:.2f} gate_up {st_med[1]:.2f} down {st_med[2]:.2f}; "
-            f"(mean) {st_mean[0]:.2f} {st_mean[1]:.2f} {st_mean[2]:.2f}")
+        def time_stages(n):
+            res = []
+            for stage in range(3):
+                gs = stage_graph(stage, n)
+                gs.replay()
+                torch.cuda.synchronize()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                reps_s = 4
+                e0.record(stream)
+                for _ in range(reps_s):
+                    gs.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                res.append(e0.elapsed_time(e1) * 1e3 / (reps_s * n))
+                del gs
+            r = np.array(res)
+            return r, r
+
+        st_med, st_mean = time_stages(max(chunk, args.stage_steps))
+        log(f"stage us per launch (graph of back-to-back launches): route {st_mean[0]:.2f} "
+            f"gate_up {st_mean[1]:.2f} down {st_mean[2]:.2f}")
         gu_bytes = (uniq if args.workload != "stack" else 8) * EXPERT_GU_BYTES + SHARED_GU_BYTES + M * 2560 * 2
         achieved = gu_bytes / (st_mean[1] * 1e-6) / 1e9
         stage = {"route": round(float(st_mean[0]), 3), "gate_up": round(float(st_mean[1]), 3),
@@ -242,6 +263,19 @@ def main():
         roof = {"bound": "hbm", "kernel": "k_gate_up (routed int4 gate_up + SiLU, shared bf16 gate_up)",
                 "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "bytes_per_launch": int(gu_bytes)}
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"calibration copy: {args.calib_copy_mib} MiB x 2")
+
+    if roof.get("traffic") is None:
+        roof["traffic"] = measured_traffic(WORKLOAD_NAMES[args.workload])
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -264,9 +298,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": {"decode": "ling_moe_layer_decode_m1", "verify2": "ling_moe_layer_verify_m2",
-                         "verify4": "ling_moe_layer_verify_m4", "stack": "ling_moe_stack40_decode_m1",
-                         "prefill": "ling_moe_layer_prefill_m4096"}[args.workload],
+            "workload": WORKLOAD_NAMES[args.workload],
             "hidden": 2560, "n_experts": 512, "top_k": 8, "moe_intermediate": 768, "group_size": 32,
             "tokens_per_step": M, "resident_layer_copies": n_layers, "graph_steps_per_replay": chunk,
             "algorithmic_bytes_per_step": int(bytes_per_step), "unique_experts_per_step": uniq,
@@ -278,6 +310,40 @@ def main():
         "build": B.build_info(),
     }
     print(json.dumps(line), flush=True)
+
+
+def kernel_sources_digest() -> str:
+    """sha256 over the HIP sources; a measured traffic figure is valid only
+    for the sources it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "w4a16_grouped_quantized_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    profile (profiles/<workload>_traffic.txt), or None when there is none or
+    the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("sources_sha256") != kernel_sources_digest():
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(shape, layer, seconds):

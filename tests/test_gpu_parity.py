@@ -262,3 +262,43 @@ def test_ling_prefill_chunk_4096_sampled(ling_big, oracle_mod):
     assert np.all((ids_g >= 0) & (ids_g < shape.n_experts))
     assert np.all(np.abs(w_g.sum(1) - 1) < 1e-5)
     _say(f"prefill 4096: sampled 48 rows, max|err|/rms = {ratio:.3e}")
+
+
+# ------------------------------------------------------------------ stacked layers
+
+@pytest.mark.parametrize("M", [1, 3])
+def test_stack_three_layers_rmsnorm_teacher_forced(ling, oracle_mod, M):
+    """Three independent Ling-shape layers, each fed the previous layer's
+    output through the fused unit-gain RMSNorm (eps 1e-6) of the routing
+    call.  Every layer is checked against the oracle on the GPU's own
+    normalised input: x_norm within one bf16 step of the oracle's RMSNorm of
+    the GPU output before it, routing within the gap band, output within
+    tolerance."""
+    import torch
+    from w4a16_grouped_quantized_amd import binding as B
+    shape = synth.LING
+    _say("generating stacked layers (seeds 2, 3)")
+    stack = [ling] + [DeviceLayer(synth.make_layer(shape, s, threads=16), max_tokens=64) for s in (2, 3)]
+    x = synth.make_tokens(shape, 60 + M, M)
+    y_dev = to_dev_bf16(x)
+    for li, dl in enumerate(stack):
+        if li == 0:
+            xin_dev = y_dev
+            ids, w = dl.route(xin_dev)
+        else:
+            xin_dev = torch.empty_like(y_dev)
+            ids, w = dl.route(y_dev, flags=B.MOE_F_INPUT_RMSNORM, x_norm=xin_dev)
+        out = dl.forward(xin_dev, ids, w)
+        torch.cuda.synchronize()
+        xin = from_dev_bf16(xin_dev)
+        if li > 0:
+            ref_norm = oracle_mod.rmsnorm(from_dev_bf16(y_dev), 1e-6)
+            diff = np.abs(xin.astype(np.int32) - ref_norm.astype(np.int32))
+            assert diff.max() <= 1, f"layer {li}: RMSNorm differs by more than one bf16 step"
+        ids_o, _, gap, logits_o = oracle_mod.route(shape, dl.layer.router_w, xin)
+        w_ref = check_ids(shape, ids.cpu().numpy(), w.cpu().numpy(), ids_o, gap, logits_o)
+        ref, bad = oracle_mod.forward(shape, dl.layer, xin, ids.cpu().numpy(), w_ref)
+        assert bad == 0
+        ratio = check_out(from_dev_bf16(out), ref, f"stack layer {li} M={M}")
+        _say(f"stack layer {li} M={M}: max|err|/rms {ratio:.3e}")
+        y_dev = out
