@@ -76,6 +76,7 @@ constexpr int kItemRows = 96;
 struct PfLayout {
   size_t err, route_cnt, shgu_cnt, dn_cnt;
   size_t logits;                    // fp32 [M][E]
+  size_t rt_planes;                 // bf16 [3][E][H] router weights split in three exact parts
   size_t counts, offsets;           // int32 [E], [E+1]
   size_t perm, inv;                 // int32 [S]: pair at each sorted position, sorted position of each pair
   size_t ghist;                     // int32 [perm_groups(S)][E]
@@ -96,6 +97,7 @@ inline PfLayout pf_layout(int H, int E, int k, int I, int has_shared, int M) {
   // sum over experts of ceil(count / kItemRows) <= E + S / kItemRows
   w.items = E + (int)((S + kItemRows - 1) / kItemRows);
   w.logits = take((size_t)M * E * 4);
+  w.rt_planes = take((size_t)3 * E * H * 2);
   w.counts = take((size_t)E * 4);
   w.offsets = take((size_t)(E + 1) * 4);
   w.perm = take(S * 4);

@@ -2,8 +2,8 @@
 // (token, slot) pairs form a dense block of rows, so the expert FFNs run as
 // grouped GEMMs on the matrix cores, fp32 accumulate throughout.
 //
-//   router:  logits[M][E] = x[M][H] * Wr^T   (Wr fp32 split exactly into three
-//            bf16 parts hi + mid + lo, one bf16 MFMA each; x is bf16)
+//   router:  logits[M][E] = x[M][H] * Wr^T   (Wr fp32 split once per call into
+//            three exact bf16 parts hi + mid + lo, one bf16 MFMA each; x is bf16)
 //   top-k:   one wavefront per token over its logits row
 //   permute: pairs grouped by expert (permute.hip), cut into work items of at
 //            most 128 rows
@@ -464,131 +464,158 @@ __global__ __launch_bounds__(kBlock, 2) void k_gg(const GgArgs a) {
 
 // ------------------------------------------------------------------ router GEMM
 
-constexpr int kRtRows = 64;          // tokens per workgroup tile
-constexpr int kRtKc = 256;           // K per LDS chunk
-constexpr int kRtStride = kRtKc + 8;
+// fp32 -> (hi, mid, lo) bf16 with hi + mid + lo == v exactly (each part
+// takes the next 8 significant bits; the rounding is to nearest even).
+__device__ __forceinline__ void split3_one(float v, uint16_t& hi, uint16_t& mid, uint16_t& lo) {
+  hi = f32_to_bf16(v);
+  const float r = v - bf16_to_f32(hi);
+  mid = f32_to_bf16(r);
+  lo = f32_to_bf16(r - bf16_to_f32(mid));
+}
+
+// The router weights [E][H] fp32 as three bf16 planes [3][E][H], once per call
+// (one thread per 8 weights).
+__global__ __launch_bounds__(kBlock) void k_rt_split(const float* __restrict__ wr, size_t n8,
+                                                     uint16_t* __restrict__ planes, size_t plane_elems) {
+  const size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x;
+  if (i >= n8) return;
+  const float4 v0 = reinterpret_cast<const float4*>(wr)[2 * i];
+  const float4 v1 = reinterpret_cast<const float4*>(wr)[2 * i + 1];
+  const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  uint16_t hh[8], mm[8], ll[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) split3_one(v[j], hh[j], mm[j], ll[j]);
+  auto pack = [](const uint16_t (&q)[8]) {
+    return make_uint4(q[0] | ((uint32_t)q[1] << 16), q[2] | ((uint32_t)q[3] << 16), q[4] | ((uint32_t)q[5] << 16),
+                      q[6] | ((uint32_t)q[7] << 16));
+  };
+  reinterpret_cast<uint4*>(planes)[i] = pack(hh);
+  reinterpret_cast<uint4*>(planes + plane_elems)[i] = pack(mm);
+  reinterpret_cast<uint4*>(planes + 2 * plane_elems)[i] = pack(ll);
+}
+
+constexpr int kRtE = 64;              // experts (MFMA rows) per workgroup
+constexpr int kRtT = 128;             // tokens per workgroup: 4 wavefronts x 32
+constexpr int kRtKc = 64;             // K per LDS chunk (one step)
+constexpr int kRtStride = kRtKc + 8;  // bf16 per LDS row (conflict-free 16-byte reads)
 
 struct RtArgs {
   int M, E, H;
-  const uint16_t* __restrict__ x;  // [M][H] bf16
-  const float* __restrict__ wr;    // [E][H] fp32
-  float* __restrict__ logits;      // [M][E]
+  const uint16_t* __restrict__ x;       // [M][H] bf16
+  const uint16_t* __restrict__ planes;  // [3][E][H] bf16
+  float* __restrict__ logits;           // [M][E]
 };
 
-// fp32 x 8 -> three bf16 x 8 parts with hi + mid + lo == v exactly.
-__device__ __forceinline__ void split3(const float (&v)[8], bf16x8_t& hi, bf16x8_t& mid, bf16x8_t& lo) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float hf = bf16_to_f32(f32_to_bf16(v[i]));
-    const float r = v[i] - hf;
-    const float mf = bf16_to_f32(f32_to_bf16(r));
-    hi[i] = __builtin_bit_cast(__bf16, f32_to_bf16(hf));
-    mid[i] = __builtin_bit_cast(__bf16, f32_to_bf16(mf));
-    lo[i] = __builtin_bit_cast(__bf16, f32_to_bf16(r - mf));
-  }
-}
-
-// Workgroup tile: 64 tokens x 256 experts (4 wavefronts x 64 router rows, as
-// two 32x32 MFMA blocks); x staged in LDS by chunks of 256 inputs; router rows
-// read a step ahead into registers and split there.
-__global__ __launch_bounds__(kBlock) void k_rt_gemm(const RtArgs a) {
-  __shared__ __align__(16) uint16_t sA[kRtRows * kRtStride];
+// logits^T block = W (64 experts x H, three bf16 parts, staged in LDS) times
+// x^T (H x 32 tokens per wavefront, loaded into registers).  The loop body
+// has no branches around memory operations: tokens past M load token M-1
+// and are not stored.
+__global__ __launch_bounds__(kBlock, 2) void k_rt_gemm(const RtArgs a) {
+  __shared__ __align__(16) uint16_t sW[2][3][kRtE * kRtStride];
   const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
-  const int j = blockIdx.x;
-  const int nvalid = min(kRtRows, a.M - kRtRows * j);
-  const int lrow = tid >> 2, lpart = tid & 3;  // 64 rows x 4 threads, 64 inputs each per chunk
-  const uint16_t* arow = a.x + (size_t)(kRtRows * j + (lrow < nvalid ? lrow : 0)) * a.H;
-  const int tile = blockIdx.y * kWavesPerBlock + wave;
-  const bool tile_ok = tile < a.E / 64;
-  const int tsafe = tile_ok ? tile : 0;
   const int n = lane & 31, h = lane >> 5;
-  f32x16_t acc[2][2];
+  const int ntE = a.E / kRtE;
+  const int et = blockIdx.x % ntE, tt = blockIdx.x / ntE;
+  const int tok = min(kRtT * tt + 32 * wave + n, a.M - 1);
+  const uint16_t* xrow = a.x + (size_t)tok * a.H + 8 * h;
+  // weight staging: 3 planes x 64 rows x 8 segments of 16 bytes = 1536 per chunk, 6 per thread
+  uint32_t soff[6];
+#pragma unroll
+  for (int j = 0; j < 6; ++j) {
+    const int q = tid + kBlock * j;
+    const int pl = q >> 9, r = (q >> 3) & 63, sg = q & 7;
+    soff[j] = (uint32_t)(((size_t)pl * a.E + kRtE * et + r) * a.H + 8 * sg);
+  }
+  // two sets of staging registers: chunk c is fetched two steps before it is
+  // stored to LDS (set c & 1)
+  uint4 wa0, wa1, wa2, wa3, wa4, wa5, wb0, wb1, wb2, wb3, wb4, wb5;
+  auto load_W = [&](int set, int kc0) {
+    const uint16_t* base = a.planes + kc0;
+    if (set == 0) {
+      wa0 = *reinterpret_cast<const uint4*>(base + soff[0]);
+      wa1 = *reinterpret_cast<const uint4*>(base + soff[1]);
+      wa2 = *reinterpret_cast<const uint4*>(base + soff[2]);
+      wa3 = *reinterpret_cast<const uint4*>(base + soff[3]);
+      wa4 = *reinterpret_cast<const uint4*>(base + soff[4]);
+      wa5 = *reinterpret_cast<const uint4*>(base + soff[5]);
+    } else {
+      wb0 = *reinterpret_cast<const uint4*>(base + soff[0]);
+      wb1 = *reinterpret_cast<const uint4*>(base + soff[1]);
+      wb2 = *reinterpret_cast<const uint4*>(base + soff[2]);
+      wb3 = *reinterpret_cast<const uint4*>(base + soff[3]);
+      wb4 = *reinterpret_cast<const uint4*>(base + soff[4]);
+      wb5 = *reinterpret_cast<const uint4*>(base + soff[5]);
+    }
+  };
+  auto store_W = [&](int set, int buf) {
+    const uint4 v[6] = {set == 0 ? wa0 : wb0, set == 0 ? wa1 : wb1, set == 0 ? wa2 : wb2,
+                        set == 0 ? wa3 : wb3, set == 0 ? wa4 : wb4, set == 0 ? wa5 : wb5};
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+      const int q = tid + kBlock * j;
+      const int pl = q >> 9, r = (q >> 3) & 63, sg = q & 7;
+      *reinterpret_cast<uint4*>(&sW[buf][pl][r * kRtStride + 8 * sg]) = v[j];
+    }
+  };
+  // x of one step: sub-step i, lane half h -> inputs 16i + 8h .. +7
+  struct XStep {
+    uint4 v[4];
+  };
+  auto load_X = [&](int kg, XStep& r) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.v[i] = *reinterpret_cast<const uint4*>(xrow + kg + 16 * i);
+  };
+  f32x16_t acc[2];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
+  const int nsteps = a.H / kRtKc;  // H % 256 == 0, so a multiple of 4
+  XStep xr[4];  // x three steps ahead
+  load_X(0, xr[0]);
+  load_X(min(1, nsteps - 1) * kRtKc, xr[1]);
+  load_X(min(2, nsteps - 1) * kRtKc, xr[2]);
+  load_W(0, 0);
+  load_W(1, min(1, nsteps - 1) * kRtKc);
+  store_W(0, 0);
+  lds_sync();
+  load_W(0, min(2, nsteps - 1) * kRtKc);
+  for (int st0 = 0; st0 < nsteps; st0 += 4) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
-  const bool two_mb = nvalid > 32;
-  struct Raw {
-    uint4 v[2][8];
-  };
-  auto load_raw = [&](int kg, Raw& r) {
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const float* wp = a.wr + (size_t)(64 * tsafe + 32 * nb + n) * a.H + kg;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        r.v[nb][2 * i] = *reinterpret_cast<const uint4*>(wp + 16 * i + 8 * h);
-        r.v[nb][2 * i + 1] = *reinterpret_cast<const uint4*>(wp + 16 * i + 8 * h + 4);
-      }
-    }
-  };
-  uint4 stage[8];
-  auto load_chunk = [&](int kc0) {
-    const uint4* src = reinterpret_cast<const uint4*>(arow + kc0 + lpart * 64);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) stage[i] = src[i];
-  };
-  auto store_chunk = [&]() {
-    uint4* dst = reinterpret_cast<uint4*>(sA + lrow * kRtStride + lpart * 64);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dst[i] = stage[i];
-  };
-  const int nsteps = a.H / 64;
-  Raw cur, nxt;
-  load_chunk(0);
-  load_raw(0, cur);
-  for (int st = 0; st < nsteps; ++st) {
-    const int kg = st * 64;
-    const int kk = kg % kRtKc;
-    if (kk == 0) {  // new LDS chunk: wait for every wavefront to finish the previous one
-      if (st > 0) lds_sync();
-      store_chunk();
-      lds_sync();
-      if (kg + kRtKc < a.H) load_chunk(kg + kRtKc);
-    }
-    if (st + 1 < nsteps) load_raw(kg + 64, nxt);
-    if (tile_ok) {
+    for (int u = 0; u < 4; ++u) {
+      const int st = st0 + u;
+      load_X(min(st + 3, nsteps - 1) * kRtKc, xr[(u + 3) & 3]);
+      const XStep& cur = xr[u];
+      const int buf = u & 1;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        bf16x8_t B[2], B2[2], B3[2];
+        const bf16x8_t B = __builtin_bit_cast(bf16x8_t, cur.v[i]);
+        // planes outer, row blocks inner: consecutive MFMAs use different accumulators
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const uint4 v0 = cur.v[nb][2 * i], v1 = cur.v[nb][2 * i + 1];
-          const float v[8] = {__uint_as_float(v0.x), __uint_as_float(v0.y), __uint_as_float(v0.z),
-                              __uint_as_float(v0.w), __uint_as_float(v1.x), __uint_as_float(v1.y),
-                              __uint_as_float(v1.z), __uint_as_float(v1.w)};
-          split3(v, B[nb], B2[nb], B3[nb]);
-        }
-        const int koff = 16 * i + 8 * h;
+        for (int pl = 0; pl < 3; ++pl) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          if (mb == 1 && !two_mb) break;
-          const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(sA + (32 * mb + n) * kRtStride + kk + koff);
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B[nb], acc[mb][nb], 0, 0, 0);
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B2[nb], acc[mb][nb], 0, 0, 0);
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B3[nb], acc[mb][nb], 0, 0, 0);
+          for (int mb = 0; mb < 2; ++mb) {
+            const bf16x8_t A =
+                *reinterpret_cast<const bf16x8_t*>(&sW[buf][pl][(32 * mb + n) * kRtStride + 16 * i + 8 * h]);
+            acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A, B, acc[mb], 0, 0, 0);
           }
         }
       }
-    }
-    cur = nxt;
-  }
-  if (!tile_ok) return;
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-    for (int sl = 0; sl < 16; ++sl) {
-      const int r = 32 * mb + c_row(lane, sl);
-      if (r >= nvalid) continue;
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-        a.logits[(size_t)(kRtRows * j + r) * a.E + 64 * tile + 32 * nb + n] = acc[mb][nb][sl];
+      // chunk st + 1 (in set (st + 1) & 1) into the other LDS buffer (its readers,
+      // step st - 1, all passed the previous barrier); then fetch chunk st + 3
+      // into the freed set
+      store_W((u + 1) & 1, buf ^ 1);
+      lds_sync();
+      load_W((u + 1) & 1, min(st + 3, nsteps - 1) * kRtKc);
     }
   }
+  const int tok_out = kRtT * tt + 32 * wave + n;
+  if (tok_out >= a.M) return;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int sl = 0; sl < 16; ++sl)
+      a.logits[(size_t)tok_out * a.E + kRtE * et + 32 * mb + c_row(lane, sl)] = acc[mb][sl];
 }
 
 // ------------------------------------------------------------------ top-k rows
@@ -765,11 +792,15 @@ static int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 hipError_t launch_prefill_route(const Shape& s, const float* router_w, const uint16_t* x, int M, int32_t* ids,
                                 float* w, uint8_t* ws, const PfLayout& P, hipStream_t st) {
-  RtArgs a{M, s.E, s.H, x, router_w, reinterpret_cast<float*>(ws + P.logits)};
-  hipLaunchKernelGGL(k_rt_gemm, dim3(ceil_div(M, kRtRows), ceil_div(s.E / 64, kWavesPerBlock)), dim3(kBlock), 0, st,
-                     a);
+  uint16_t* planes = reinterpret_cast<uint16_t*>(ws + P.rt_planes);
+  const size_t plane = (size_t)s.E * s.H, n8 = plane / 8;
+  hipLaunchKernelGGL(k_rt_split, dim3((unsigned)((n8 + kBlock - 1) / kBlock)), dim3(kBlock), 0, st, router_w, n8,
+                     planes, plane);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  RtArgs a{M, s.E, s.H, x, planes, reinterpret_cast<float*>(ws + P.logits)};
+  hipLaunchKernelGGL(k_rt_gemm, dim3((unsigned)((s.E / kRtE) * ceil_div(M, kRtT))), dim3(kBlock), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   TopkArgs t{M, s.E, s.k, a.logits, ids, w};
   hipLaunchKernelGGL(k_topk_rows, dim3(ceil_div(M, kWavesPerBlock)), dim3(kBlock), 0, st, t);
   return hipGetLastError();
