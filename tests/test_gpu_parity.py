@@ -302,3 +302,33 @@ def test_stack_three_layers_rmsnorm_teacher_forced(ling, oracle_mod, M):
         ratio = check_out(from_dev_bf16(out), ref, f"stack layer {li} M={M}")
         _say(f"stack layer {li} M={M}: max|err|/rms {ratio:.3e}")
         y_dev = out
+
+
+def test_ling_many_tokens_caller_ids(ling_big, oracle_mod):
+    """The grouped-GEMM path with caller ids: duplicates inside a token, ids
+    out of range (error word, zero contribution), one expert taking every
+    token (more rows than one work item) and experts with no token at all."""
+    import torch
+    shape = synth.LING
+    M = 200
+    x = synth.make_tokens(shape, 91, M)
+    rng = np.random.default_rng(91)
+    ids = rng.integers(0, 64, size=(M, shape.top_k)).astype(np.int32)   # experts 64.. get no token
+    ids[:, 0] = 7                      # expert 7 in every token: 200+ rows, three work items
+    ids[5, 1] = ids[5, 2] = 9          # duplicate inside one token
+    w = rng.random((M, shape.top_k)).astype(np.float32)
+    out = ling_big.forward(to_dev_bf16(x), torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda())
+    torch.cuda.synchronize()
+    assert ling_big.device_error() == 0
+    ref, bad = oracle_mod.forward(shape, ling_big.layer, x, ids, w.astype(np.float64))
+    assert bad == 0
+    check_out(from_dev_bf16(out), ref, "many tokens, caller ids")
+    ids_bad = ids.copy()
+    ids_bad[3, 4] = 512
+    ids_bad[150, 0] = -2
+    out = ling_big.forward(to_dev_bf16(x), torch.from_numpy(ids_bad).cuda(), torch.from_numpy(w).cuda())
+    torch.cuda.synchronize()
+    assert ling_big.device_error() == 1
+    ref, bad = oracle_mod.forward(shape, ling_big.layer, x, ids_bad, w.astype(np.float64))
+    assert bad == 2
+    check_out(from_dev_bf16(out), ref, "many tokens, invalid ids contribute zero")
