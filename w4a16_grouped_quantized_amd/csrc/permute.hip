@@ -38,6 +38,37 @@ __global__ __launch_bounds__(kPermThreads) void k_perm_count(const int32_t* __re
   if (tid == 0 && bad) atomicOr(err, 1);
 }
 
+// Exclusive scan over v[0..n) in LDS (n <= kPermThreads), whole workgroup;
+// v[n] receives the total.  Wavefront prefix sums with shuffles, then a scan
+// of the wavefront totals.
+__device__ void block_exclusive_scan(int* v, int n, int* wsum) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int x = tid < n ? v[tid] : 0;
+  int inc = x;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(inc, off, kWave);
+    if (lane >= off) inc += y;
+  }
+  if (lane == kWave - 1) wsum[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    const int t = lane < kPermWaves ? wsum[lane] : 0;
+    int ti = t;
+#pragma unroll
+    for (int off = 1; off < kPermWaves; off <<= 1) {
+      const int y = __shfl_up(ti, off, kWave);
+      if (lane >= off) ti += y;
+    }
+    if (lane < kPermWaves) wsum[lane] = ti - t;  // exclusive over wavefronts
+    if (lane == kPermWaves - 1) wsum[kPermWaves] = ti;
+  }
+  __syncthreads();
+  if (tid < n) v[tid] = wsum[wave] + inc - x;
+  if (tid == 0) v[n] = wsum[kPermWaves];
+  __syncthreads();
+}
+
 struct PermOut {
   int32_t* counts;   // [E]
   int32_t* offsets;  // [E+1]
@@ -52,7 +83,8 @@ __global__ __launch_bounds__(kPermThreads) void k_perm_scatter(const int32_t* __
                                                                const int32_t* __restrict__ ghist, PermOut o) {
   __shared__ int whist[kPermWaves][kMaxExperts];
   __shared__ int start[kMaxExperts + 1];  // exclusive scan of the totals
-  __shared__ int mine[kMaxExperts];       // this workgroup's base inside each expert's run
+  __shared__ int mine[kMaxExperts + 1];   // this workgroup's base inside each expert's run
+  __shared__ int wsum[kPermWaves + 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = blockIdx.x, G = gridDim.x;
   for (int e = tid; e < E; e += kPermThreads) {
@@ -67,15 +99,7 @@ __global__ __launch_bounds__(kPermThreads) void k_perm_scatter(const int32_t* __
   }
   for (int i = tid; i < kPermWaves * kMaxExperts; i += kPermThreads) (&whist[0][0])[i] = 0;
   __syncthreads();
-  if (tid == 0) {  // E <= 512: a serial scan is a few hundred cycles
-    int run = 0;
-    for (int e = 0; e < E; ++e) {
-      const int c = start[e];
-      start[e] = run;
-      run += c;
-    }
-    start[E] = run;
-  }
+  block_exclusive_scan(start, E, wsum);
   const int lo = g * kPermSeg + wave * kPermSub;
   const int hi = min(S, lo + kPermSub);
   for (int p = lo + lane; p < hi; p += kWave) {
@@ -123,16 +147,10 @@ __global__ __launch_bounds__(kPermThreads) void k_perm_scatter(const int32_t* __
   if (o.tile_e == nullptr) return;
   // work items: expert e owns ceil(count_e / kItemRows) consecutive items
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int e = 0; e < E; ++e) {
-      const int c = start[e + 1] - start[e];
-      mine[e] = run;  // reused: first item of expert e
-      run += (c + kItemRows - 1) / kItemRows;
-    }
-    *o.ntile = run;
-  }
+  if (tid < E) mine[tid] = (start[tid + 1] - start[tid] + kItemRows - 1) / kItemRows;  // reused: items of e
   __syncthreads();
+  block_exclusive_scan(mine, E, wsum);  // first item of each expert; mine[E] = total
+  if (tid == 0) *o.ntile = mine[E];
   for (int e = tid; e < E; e += kPermThreads) {
     const int n = (start[e + 1] - start[e] + kItemRows - 1) / kItemRows;
     for (int j = 0; j < n; ++j) {
