@@ -84,7 +84,7 @@ struct PfLayout {
   size_t xh, rexp;                  // fp16 [M][H] scaled rows of x, int32 [M] their exponents
   size_t hbuf;                      // fp16 [S][I] scaled h per sorted position
   size_t hsh;                       // bf16 [2][M][I] shared-expert h as (hi, lo) planes
-  size_t y, ysh;                    // fp32 [S][H] per sorted position, [M][H]
+  size_t y, ysh;                    // fp16 [S][H] per sorted position (scaled), fp32 [M][H]
   size_t total;
   int items;                        // bound on the routed work items
 };
@@ -110,7 +110,7 @@ inline PfLayout pf_layout(int H, int E, int k, int I, int has_shared, int M) {
   w.rexp = take((size_t)M * 4);
   w.hbuf = take(S * I * 2);
   w.hsh = take(has_shared ? (size_t)2 * M * I * 2 : 0);
-  w.y = take(S * H * 4);
+  w.y = take(S * H * 2);
   w.ysh = take(has_shared ? (size_t)M * H * 4 : 0);
   w.total = off;
   return w;

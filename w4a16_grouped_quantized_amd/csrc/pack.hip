@@ -112,16 +112,37 @@ __global__ __launch_bounds__(256) void k_pack_meta_gu(const uint8_t* __restrict_
   }
 }
 
-// Largest |scale| of each expert's down matrix into word 1.
-__global__ __launch_bounds__(256) void k_pack_meta_dn(const uint16_t* __restrict__ sc, uint32_t* __restrict__ meta,
-                                                      size_t per_e) {
+// One wavefront per down row n of one expert (lane l takes groups l, l + 64,
+// ...): the row's dequantised L1 norm into word 3 (max over rows) and the
+// largest |scale| into word 1.
+__global__ __launch_bounds__(256) void k_pack_meta_dn(const uint8_t* __restrict__ q, const uint16_t* __restrict__ sc,
+                                                      uint32_t* __restrict__ meta, int H, int I) {
   const int e = blockIdx.y;
-  float m = 0.f;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < per_e; i += (size_t)gridDim.x * blockDim.x)
-    m = fmaxf(m, fabsf(bf16_to_f32(sc[(size_t)e * per_e + i])));
+  const int r = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= H) return;
+  const int GK = I / kGroup;
+  const size_t row = (size_t)e * H + r;
+  float norm = 0.f, smax = 0.f;
+  for (int g = lane; g < GK; g += kWave) {
+    const uint4 w = *reinterpret_cast<const uint4*>(q + row * (I / 2) + (size_t)g * 16);
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    int sum = 0;
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  if ((threadIdx.x & 63) == 0) max_bits(meta + (size_t)e * kMetaWords + 1, m);
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int n = 0; n < 8; ++n) sum += abs((int)((wd[d] >> (4 * n)) & 0xFu) - 8);
+    const float s = fabsf(bf16_to_f32(sc[row * GK + g]));
+    norm += s * (float)sum;
+    smax = fmaxf(smax, s);
+  }
+  norm = wave_sum(norm);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) smax = fmaxf(smax, __shfl_xor(smax, off, 64));
+  if (lane == 0) {
+    max_bits(meta + (size_t)e * kMetaWords + 1, smax);
+    max_bits(meta + (size_t)e * kMetaWords + 3, norm);
+  }
 }
 
 __global__ void k_fill_zero(uint4* __restrict__ p, size_t n16, uint8_t* __restrict__ tail, size_t ntail) {
@@ -165,7 +186,8 @@ hipError_t launch_pack(const Shape& s, const uint8_t* w13_q, const uint16_t* w13
   hipLaunchKernelGGL(k_pack_meta_gu, dim3((I + kWavesPerBlock - 1) / kWavesPerBlock, E), dim3(256), 0, st, w13_q,
                      w13_s, meta, H, I);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(k_pack_meta_dn, dim3(8, E), dim3(256), 0, st, w2_s, meta, (size_t)H * (I / kGroup));
+  hipLaunchKernelGGL(k_pack_meta_dn, dim3((H + kWavesPerBlock - 1) / kWavesPerBlock, E), dim3(256), 0, st, w2_q, w2_s,
+                     meta, H, I);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (s.has_shared) {
     n = (size_t)(2 * I / 64) * (H / 8) * kWave;

@@ -13,7 +13,8 @@
 //   gate_up: per item, rows x[token] times the INT4 gate/up rows dequantised
 //            to fp16 as q * s * 2^p; h = silu(gate) * up, stored as fp16
 //            scaled by 2^-sigma with sigma from a bound on |h| (below)
-//   down:    h times the INT4 down rows, one fp32 row per sorted pair
+//   down:    h times the INT4 down rows, one fp16 row per sorted pair under a
+//            per-expert power-of-two scale (|y| <= ||down row||_1 max|h|)
 //   shared:  the same two GEMMs on all tokens with the BF16 shared weights in
 //            bf16 MFMAs (x as is, h as an exact-to-16-bits hi + lo pair)
 //   combine: out[t] = sum_j w[t][j] * y[pair (t, j)] + y_shared[t], slot order
@@ -133,7 +134,7 @@ struct GgArgs {
   // outputs
   _Float16* __restrict__ hout;        // [S][I]
   uint16_t* __restrict__ hsh_out;     // [2][M][I]
-  float* __restrict__ y;              // [S][H]
+  _Float16* __restrict__ y;           // [S][H] y * 2^-(sigma + e2 - 1), e2 from the down-row norm bound
   float* __restrict__ ysh;            // [M][H]
 };
 
@@ -161,6 +162,7 @@ __device__ __forceinline__ uint32_t dword_of(const uint4& v, int i) {
 // Everything a workgroup knows about its item once the row tables are built.
 struct GgItem {
   int e, base, nrow, p;
+  int ey;  // down: exponent that takes the accumulators to the stored fp16 y
 };
 
 // Main loop and epilogue for items of NMB 32-row blocks.  The loop body has
@@ -379,10 +381,11 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgItem& it, uint16
         const int col = 32 * t + n;
         a.hout[(size_t)(it.base + r) * a.I + (col & ~7) + k8_pos(col & 7)] = (_Float16)hv;
       } else if constexpr (KIND == GG_RDN) {
-        const int ex = sExp[r] - it.p;
+        // acc = y 2^(p - sigma) and |y| < 2^(sigma + 13 + e2): the stored
+        // y 2^-(sigma + e2 - 1) = acc 2^(1 - p - e2) stays below 2^14
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb)
-          a.y[(size_t)(it.base + r) * a.H + 64 * t + 32 * nb + n] = ldexpf(acc[mb][nb][sl], ex);
+          a.y[(size_t)(it.base + r) * a.H + 64 * t + 32 * nb + n] = (_Float16)ldexpf(acc[mb][nb][sl], it.ey);
       } else if constexpr (KIND == GG_SGU) {
         const float hv = silu_f32(acc[mb][0][sl]) * acc[mb][1][sl];
         const uint16_t hi = f32_to_bf16(hv), lo = f32_to_bf16(hv - bf16_to_f32(hi));
@@ -414,7 +417,7 @@ __global__ __launch_bounds__(kBlock, 2) void k_gg(const GgArgs a) {
   // ---- work item
   const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
   const int item = (slot / a.ng) * 8 + xcd;
-  GgItem it{0, 0, 0, 0};
+  GgItem it{0, 0, 0, 0, 0};
   if constexpr (C::ROUTED) {
     if (item >= uniform(a.ntile[0])) return;
     it.e = uniform(a.tile_e[item]);
@@ -431,6 +434,7 @@ __global__ __launch_bounds__(kBlock, 2) void k_gg(const GgArgs a) {
     const uint32_t* mt = a.meta + (size_t)it.e * kMetaWords;
     it.p = min(12 - exp_above(__uint_as_float(mt[a.meta_word])), 126);
     ne = exp_above(__uint_as_float(mt[2])) + 1;
+    it.ey = 1 - it.p - exp_above(__uint_as_float(mt[3]));
   }
   // ---- row tables: A source row and the exponents of each row
   if (tid < C::ROWS) {
@@ -743,15 +747,18 @@ struct CombineArgs {
   int M, E, k, H, has_shared;
   const int32_t* __restrict__ ids;
   const float* __restrict__ topk_w;
-  const int32_t* __restrict__ inv;  // sorted position of each pair
-  const float* __restrict__ y;      // [S][H] per sorted position
+  const int32_t* __restrict__ inv;     // sorted position of each pair
+  const _Float16* __restrict__ y;      // [S][H] per sorted position, scaled (see GgArgs::y)
+  const int32_t* __restrict__ rexp;    // [M] row exponents of x
+  const uint32_t* __restrict__ meta;   // per-expert range data
   const float* __restrict__ ysh;    // [M][H]
   uint16_t* __restrict__ out;
   int32_t* __restrict__ err;
 };
 
-// One thread per 4 outputs of one token: the y rows of the token's k slots
-// are summed in slot order, then the shared expert's row.
+// One thread per 4 outputs of one token: the y rows of the token's k slots,
+// each back at its true scale 2^(sigma + e2 - 1) and weighted, are summed in
+// slot order, then the shared expert's row.
 __global__ __launch_bounds__(kBlock) void k_pf_combine(const CombineArgs a) {
   const size_t q = (size_t)blockIdx.x * kBlock + threadIdx.x;  // quad index
   const size_t per_tok = a.H / 4;
@@ -764,10 +771,13 @@ __global__ __launch_bounds__(kBlock) void k_pf_combine(const CombineArgs a) {
     const int p = t * a.k + jj;
     const int e = a.ids[p];
     if (e < 0 || e >= a.E) { bad = true; continue; }
-    const float wv = a.topk_w[p];
-    const float4 v = *reinterpret_cast<const float4*>(a.y + (size_t)a.inv[p] * a.H + n0);
-    acc.x = fmaf(wv, v.x, acc.x); acc.y = fmaf(wv, v.y, acc.y);
-    acc.z = fmaf(wv, v.z, acc.z); acc.w = fmaf(wv, v.w, acc.w);
+    const uint32_t* mt = a.meta + (size_t)e * kMetaWords;
+    const int sigma = 2 * a.rexp[t] + 16 + exp_above(__uint_as_float(mt[2])) + 1;
+    const float wv = ldexpf(a.topk_w[p], sigma + exp_above(__uint_as_float(mt[3])) - 1);
+    const uint2 raw = *reinterpret_cast<const uint2*>(a.y + (size_t)a.inv[p] * a.H + n0);
+    const f16x2_t v01 = __builtin_bit_cast(f16x2_t, raw.x), v23 = __builtin_bit_cast(f16x2_t, raw.y);
+    acc.x = fmaf(wv, (float)v01[0], acc.x); acc.y = fmaf(wv, (float)v01[1], acc.y);
+    acc.z = fmaf(wv, (float)v23[0], acc.z); acc.w = fmaf(wv, (float)v23[1], acc.w);
   }
   if (a.has_shared) {
     const float4 v = *reinterpret_cast<const float4*>(a.ysh + (size_t)t * a.H + n0);
@@ -833,7 +843,7 @@ hipError_t launch_prefill_forward(const Shape& s, const uint8_t* packed, const P
   a.meta = reinterpret_cast<const uint32_t*>(packed + PL.meta);
   a.hout = reinterpret_cast<_Float16*>(ws + P.hbuf);
   a.hsh_out = reinterpret_cast<uint16_t*>(ws + P.hsh);
-  a.y = reinterpret_cast<float*>(ws + P.y);
+  a.y = reinterpret_cast<_Float16*>(ws + P.y);
   a.ysh = reinterpret_cast<float*>(ws + P.ysh);
   // gate_up
   a.K = s.H;
@@ -863,7 +873,7 @@ hipError_t launch_prefill_forward(const Shape& s, const uint8_t* packed, const P
     hipLaunchKernelGGL(k_gg<GG_SDN>, gg_grid(ceil_div(M, GgCfg<GG_SDN>::ROWS), a.ng), dim3(kBlock), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  CombineArgs c{M, s.E, s.k, s.H, s.has_shared, ids, w, i32(P.inv), a.y, a.ysh, out, err};
+  CombineArgs c{M, s.E, s.k, s.H, s.has_shared, ids, w, i32(P.inv), a.y, i32(P.rexp), a.meta, a.ysh, out, err};
   const size_t quads = (size_t)M * (s.H / 4);
   hipLaunchKernelGGL(k_pf_combine, dim3((unsigned)((quads + kBlock - 1) / kBlock)), dim3(kBlock), 0, st, c);
   return hipGetLastError();
