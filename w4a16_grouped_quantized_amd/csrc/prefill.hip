@@ -163,6 +163,7 @@ __device__ __forceinline__ uint32_t dword_of(const uint4& v, int i) {
 struct GgItem {
   int e, base, nrow, p;
   int ey;  // down: exponent that takes the accumulators to the stored fp16 y
+  int yb;  // group of 4 weight tiles of this workgroup
 };
 
 // Main loop and epilogue for items of NMB 32-row blocks.  The loop body has
@@ -233,7 +234,7 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgItem& it, uint16
     });
   };
   // ---- this wavefront's weight tile (tiles past the last read tile 0 and are dropped)
-  const int t = (int)(blockIdx.x >> 3) % a.ng * kWavesPerBlock + wave;
+  const int t = it.yb * kWavesPerBlock + wave;
   const bool tile_ok = t < a.ntiles;
   const int tt = tile_ok ? t : 0;
   const int GK = a.K / kGroup;
@@ -407,17 +408,14 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgItem& it, uint16
 // run back to back on one XCD (ids are dealt to the 8 XCDs round-robin), so
 // the item's activation rows are read from that XCD's L2 after the first.
 template <int KIND>
-__global__ __launch_bounds__(kBlock, 2) void k_gg(const GgArgs a) {
+__device__ __forceinline__ void gg_item(const GgArgs& a, int b, uint16_t (*sA)[kGgLdsRows * kGgStride], int* sSrc,
+                                        int* sExp, int* sSig) {
   using C = GgCfg<KIND>;
-  __shared__ __align__(16) uint16_t sA[2][kGgLdsRows * kGgStride];
-  __shared__ int sSrc[C::ROWS];
-  __shared__ int sExp[C::ROWS];
-  __shared__ int sSig[C::ROWS];
   const int tid = threadIdx.x;
-  // ---- work item
-  const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
+  // ---- work item (b: this launch part's workgroup index)
+  const int xcd = b & 7, slot = b >> 3;
   const int item = (slot / a.ng) * 8 + xcd;
-  GgItem it{0, 0, 0, 0, 0};
+  GgItem it{0, 0, 0, 0, 0, slot % a.ng};
   if constexpr (C::ROUTED) {
     if (item >= uniform(a.ntile[0])) return;
     it.e = uniform(a.tile_e[item]);
@@ -464,6 +462,25 @@ __global__ __launch_bounds__(kBlock, 2) void k_gg(const GgArgs a) {
     if (nmb == 1) gg_run<KIND, 1>(a, it, sA, sSrc, sExp, sSig);
     else gg_run<KIND, 2>(a, it, sA, sSrc, sExp, sSig);
   }
+}
+
+template <int KIND>
+__global__ __launch_bounds__(kBlock, 2) void k_gg(const GgArgs a) {
+  __shared__ __align__(16) uint16_t sA[2][kGgLdsRows * kGgStride];
+  __shared__ int sSrc[kGgLdsRows], sExp[kGgLdsRows], sSig[kGgLdsRows];
+  gg_item<KIND>(a, blockIdx.x, sA, sSrc, sExp, sSig);
+}
+
+// The routed and the shared GEMM of one phase in one launch: the shared work
+// items take the workgroup ids after the routed ones (whose count is a
+// multiple of 8, so the XCD mapping of each part is kept) and fill the tail
+// of the routed part.
+template <int KR, int KS>
+__global__ __launch_bounds__(kBlock, 2) void k_gg2(const GgArgs a, int routed_blocks) {
+  __shared__ __align__(16) uint16_t sA[2][kGgLdsRows * kGgStride];
+  __shared__ int sSrc[kGgLdsRows], sExp[kGgLdsRows], sSig[kGgLdsRows];
+  if ((int)blockIdx.x < routed_blocks) gg_item<KR>(a, blockIdx.x, sA, sSrc, sExp, sSig);
+  else gg_item<KS>(a, blockIdx.x - routed_blocks, sA, sSrc, sExp, sSig);
 }
 
 // ------------------------------------------------------------------ router GEMM
@@ -853,12 +870,14 @@ hipError_t launch_prefill_forward(const Shape& s, const uint8_t* packed, const P
   a.q_stride = PL.gu_q_stride; a.s_stride = PL.gu_s_stride / 2; a.P = kg.P; a.pshift = kg.P == 4 ? 2 : kg.P - 1;
   a.shw = reinterpret_cast<const uint16_t*>(packed + PL.sh_gu);
   a.meta_word = 0;
-  hipLaunchKernelGGL(k_gg<GG_RGU>, gg_grid(P.items, a.ng), dim3(kBlock), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (s.has_shared) {
-    hipLaunchKernelGGL(k_gg<GG_SGU>, gg_grid(ceil_div(M, GgCfg<GG_SGU>::ROWS), a.ng), dim3(kBlock), 0, st, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int rb = (int)gg_grid(P.items, a.ng).x;
+    const int sb = (int)gg_grid(ceil_div(M, GgCfg<GG_SGU>::ROWS), a.ng).x;
+    hipLaunchKernelGGL((k_gg2<GG_RGU, GG_SGU>), dim3(rb + sb), dim3(kBlock), 0, st, a, rb);
+  } else {
+    hipLaunchKernelGGL(k_gg<GG_RGU>, gg_grid(P.items, a.ng), dim3(kBlock), 0, st, a);
   }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   // down
   a.K = s.I;
   a.ntiles = s.H / 64;
@@ -867,12 +886,14 @@ hipError_t launch_prefill_forward(const Shape& s, const uint8_t* packed, const P
   a.q_stride = PL.dn_q_stride; a.s_stride = PL.dn_s_stride / 2; a.P = kd.P; a.pshift = kd.P == 4 ? 2 : kd.P - 1;
   a.shw = reinterpret_cast<const uint16_t*>(packed + PL.sh_dn);
   a.meta_word = 1;
-  hipLaunchKernelGGL(k_gg<GG_RDN>, gg_grid(P.items, a.ng), dim3(kBlock), 0, st, a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (s.has_shared) {
-    hipLaunchKernelGGL(k_gg<GG_SDN>, gg_grid(ceil_div(M, GgCfg<GG_SDN>::ROWS), a.ng), dim3(kBlock), 0, st, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int rb = (int)gg_grid(P.items, a.ng).x;
+    const int sb = (int)gg_grid(ceil_div(M, GgCfg<GG_SDN>::ROWS), a.ng).x;
+    hipLaunchKernelGGL((k_gg2<GG_RDN, GG_SDN>), dim3(rb + sb), dim3(kBlock), 0, st, a, rb);
+  } else {
+    hipLaunchKernelGGL(k_gg<GG_RDN>, gg_grid(P.items, a.ng), dim3(kBlock), 0, st, a);
   }
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   CombineArgs c{M, s.E, s.k, s.H, s.has_shared, ids, w, i32(P.inv), a.y, i32(P.rexp), a.meta, a.ysh, out, err};
   const size_t quads = (size_t)M * (s.H / 4);
   hipLaunchKernelGGL(k_pf_combine, dim3((unsigned)((quads + kBlock - 1) / kBlock)), dim3(kBlock), 0, st, c);
