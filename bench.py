@@ -64,6 +64,9 @@ def parse():
     p.add_argument("--copies", type=int, default=None,
                    help="resident layer copies to rotate over (default 32; 1 for prefill, which reads every expert)")
     p.add_argument("--chunk", type=int, default=256, help="steps captured per graph")
+    p.add_argument("--path", default="layer", choices=["layer", "calls"],
+                   help="layer: one moe_layer_w4a16 call per layer step (one launch at small M); "
+                        "calls: moe_route then moe_forward_w4a16")
     p.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--stage-steps", type=int, default=256, help="eager steps timed per stage")
@@ -126,6 +129,7 @@ def main():
     w = torch.empty((chunk, M, shape.top_k), dtype=torch.float32, device="cuda")
     out = torch.empty((chunk, M, shape.hidden), dtype=torch.bfloat16, device="cuda")
     xn = torch.empty((chunk, M, shape.hidden), dtype=torch.bfloat16, device="cuda")
+    out2 = torch.empty((chunk, M, shape.hidden), dtype=torch.bfloat16, device="cuda")
 
     def run_steps(lo, hi, step_offset):
         """Enqueue steps lo..hi-1 (the graph body)."""
@@ -136,7 +140,15 @@ def main():
                 x_in = X[i * M:(i + 1) * M]
                 for l in range(n_layers):
                     pk, rt = copies[l]
-                    if l == 0:
+                    if args.path == "layer":
+                        # outputs alternate between two buffers: layer l reads layer l-1's
+                        bufs = (out[i], out2[i])
+                        if l == 0:
+                            B.layer(cfg, rt, pk, x_in, ids[i], w[i], bufs[0], ws.buf)
+                        else:
+                            B.layer(cfg, rt, pk, bufs[(l - 1) % 2], ids[i], w[i], bufs[l % 2], ws.buf,
+                                    flags=B.MOE_F_INPUT_RMSNORM, x_norm=xn[i])
+                    elif l == 0:
                         B.route(cfg, rt, x_in, ids[i], w[i], ws.buf)
                         B.forward(cfg, pk, x_in, ids[i], w[i], out[i], ws.buf)
                     else:
@@ -145,8 +157,11 @@ def main():
             else:
                 pk, rt = copies[s % n_layers]
                 x_in = X[i * M:(i + 1) * M]
-                B.route(cfg, rt, x_in, ids[i], w[i], ws.buf)
-                B.forward(cfg, pk, x_in, ids[i], w[i], out[i], ws.buf)
+                if args.path == "layer":
+                    B.layer(cfg, rt, pk, x_in, ids[i], w[i], out[i], ws.buf)
+                else:
+                    B.route(cfg, rt, x_in, ids[i], w[i], ws.buf)
+                    B.forward(cfg, pk, x_in, ids[i], w[i], out[i], ws.buf)
 
     # warm the stream outside capture, then capture one chunk
     run_steps(0, chunk, 0)

@@ -32,6 +32,11 @@
  *  - Data errors seen on the device (an expert id outside [0, n_experts))
  *    set a sticky error word in the workspace and the affected slot
  *    contributes zero; moe_get_device_error reports it.
+ *  - The one-launch small-M path hands data between workgroups of one grid
+ *    through flags and counters in the workspace; a hand-off that does not
+ *    complete within its bounded wait sets bit 1 of the error word (the
+ *    result of that call is then undefined, and the workspace must be
+ *    re-initialised with moe_workspace_init).
  */
 #ifndef MOE_W4A16_H
 #define MOE_W4A16_H
@@ -124,6 +129,19 @@ int moe_forward_w4a16(const moe_config* cfg /* host */, const void* packed, cons
                       int32_t M, const int32_t* topk_ids, const float* topk_w, uint16_t* out,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* One whole layer for a step of M tokens: moe_route followed by
+ * moe_forward_w4a16 on the ids and weights it produced, with the same
+ * results (topk_ids, topk_w, x_norm and out are all written).  For small M
+ * (M*top_k <= 64, the decode and verify steps) the router, the top-k and the
+ * expert FFNs run as one launch whose routed weight loads start as soon as
+ * the experts are chosen; otherwise it is the two calls.  flags as for
+ * moe_route (with MOE_F_INPUT_RMSNORM the experts see x_norm).
+ * M = 0 is a no-op. */
+int moe_layer_w4a16(const moe_config* cfg /* host */, const float* router_w, const void* packed,
+                    const uint16_t* x, int32_t M, uint32_t flags, uint16_t* x_norm,
+                    int32_t* topk_ids, float* topk_w, uint16_t* out,
+                    void* ws, size_t ws_bytes, void* stream);
+
 /* The two stages of moe_forward_w4a16, for callers that schedule them
  * separately (moe_forward_w4a16 = moe_gate_up_w4a16 then moe_down_w4a16 on
  * the same workspace, stream, M and topk_ids).
@@ -148,7 +166,8 @@ int moe_permute(const moe_config* cfg /* host */, const int32_t* topk_ids, int32
                 void* ws, size_t ws_bytes, void* stream);
 
 /* Synchronise `stream`, read the sticky device error word into *code_host
- * (0 = none; bit 0 = an expert id outside [0, E) was seen) and clear it.
+ * (0 = none; bit 0 = an expert id outside [0, E) was seen; bit 1 = a
+ * hand-off inside a one-launch layer timed out) and clear it.
  * Returns MOE_OK, or MOE_ERR_DEVICE when the word was non-zero. */
 int moe_get_device_error(void* ws, void* stream, int32_t* code_host /* host */);
 

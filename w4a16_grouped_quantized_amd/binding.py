@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_E
 
 # Every symbol include/moe_w4a16.h declares.
 EXPORTS = ("moe_packed_size", "moe_pack_weights", "moe_workspace_size", "moe_workspace_init",
-           "moe_route", "moe_forward_w4a16", "moe_gate_up_w4a16", "moe_down_w4a16", "moe_permute",
+           "moe_route", "moe_forward_w4a16", "moe_layer_w4a16", "moe_gate_up_w4a16", "moe_down_w4a16", "moe_permute",
            "moe_get_device_error", "moe_status_string", "moe_build_info")
 
 
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
             L.moe_route.argtypes = [cfgp, _P, _P, ctypes.c_int32, ctypes.c_uint32, _P, _P, _P, _P,
                                     ctypes.c_size_t, _P]
             L.moe_forward_w4a16.argtypes = [cfgp, _P, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t, _P]
+            L.moe_layer_w4a16.argtypes = [cfgp, _P, _P, _P, ctypes.c_int32, ctypes.c_uint32, _P, _P, _P, _P, _P,
+                                          ctypes.c_size_t, _P]
             L.moe_gate_up_w4a16.argtypes = [cfgp, _P, _P, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]
             L.moe_down_w4a16.argtypes = [cfgp, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t, _P]
             L.moe_permute.argtypes = [cfgp, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t, _P]
@@ -141,6 +143,13 @@ def forward(cfg, packed, x, topk_ids, topk_w, out, ws, stream=None):
     _check("moe_forward_w4a16", lib().moe_forward_w4a16(ctypes.byref(cfg), _ptr(packed), _ptr(x), M,
                                                         _ptr(topk_ids), _ptr(topk_w), _ptr(out), _ptr(ws),
                                                         ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def layer(cfg, router_w, packed, x, topk_ids, topk_w, out, ws, flags: int = 0, x_norm=None, stream=None):
+    M = x.shape[0]
+    _check("moe_layer_w4a16", lib().moe_layer_w4a16(ctypes.byref(cfg), _ptr(router_w), _ptr(packed), _ptr(x), M,
+                                                    flags, _ptr(x_norm), _ptr(topk_ids), _ptr(topk_w), _ptr(out),
+                                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def gate_up(cfg, packed, x, topk_ids, ws, stream=None):

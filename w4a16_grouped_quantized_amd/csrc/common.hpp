@@ -8,21 +8,6 @@
 
 namespace moe {
 
-// Workspace: counters and the sticky error word first, then the per-call
-// scratch arrays, each 256-byte aligned.
-struct WsLayout {
-  size_t err, route_cnt, shgu_cnt, dn_cnt;   // int32 words
-  size_t logits;                             // fp32 [Mmax][E]
-  size_t h;                                  // bf16 [Mmax*k][I]
-  size_t h_sh;                               // bf16 [Mmax][I]
-  size_t shgu_part;                          // fp32 [Mmax][Tgu][KSgu][64]
-  size_t dpart;                              // fp32 [Mmax*k][H]
-  size_t shdn_part;                          // fp32 [Mmax][KSdn][H]
-  size_t ghist;                              // int32 [perm_groups(Mmax*k)][E] (moe_permute)
-  size_t total;
-  int Tgu, Tdn, KSgu, KSdn, CWgu, CWdn;
-};
-
 // The shared expert's K split targets the same bytes per wavefront as the
 // routed matrix of the same phase (its K-groups per wavefront).
 inline SharedSplit shared_gu_split(int H) { return shared_split_for(H, ksplit_for(H / kGroup).GW); }
@@ -33,18 +18,96 @@ inline SharedSplit shared_dn_split(int I) { return shared_split_for(I, ksplit_fo
 constexpr int kPermSeg = 2048;
 inline int perm_groups(long long S) { return (int)((S + kPermSeg - 1) / kPermSeg); }
 
-// Both paths share one header: the error word at offset 0 and the decode
-// path's arrival counters, which must stay zero between calls whichever path
-// ran last.  Per-call arrays follow the header.
-inline size_t ws_header(int H, int I, size_t* err, size_t* route_cnt, size_t* shgu_cnt, size_t* dn_cnt) {
+// Arrival counters are kCntStride ints apart (256 bytes): atomics on one
+// line are serialised, so counters that fill at the same time never share one.
+constexpr int kCntStride = 64;
+// Last-arriver trees: groups of kArriveFan workgroups count on their own
+// counter, the last of each group on a top counter.
+constexpr int kArriveFan = 16;
+// Distinct-expert units of the one-launch small-M layer (M*k <= this).
+constexpr int kMaxUnits = 64;
+// Router workgroups (4 rows each) of up to 512 experts: one top counter and
+// one per group of kArriveFan.
+constexpr int kRouteCounters = 1 + (512 / 4 + kArriveFan - 1) / kArriveFan;
+
+// Both paths share one header: the error word at offset 0 and the small-M
+// path's arrival counters, which must stay zero between calls whichever
+// path ran last (each counter is reset by the workgroup that completes it).
+// Per-call arrays follow the header.
+struct WsHeader {
+  size_t err;        // int32 sticky error word
+  size_t route_cnt;  // int32 [kRouteCounters] spaced: top counter, then one per group
+  size_t shgu_cnt;   // int32 [I/32] spaced: K slices finished per shared gate_up tile
+  size_t dn_cnt;     // int32 [H/64] spaced: partial rows finished per down tile
+  size_t hcnt;       // int32 [kMaxUnits] spaced: gate_up tiles finished per routed unit
+  size_t shdone;     // int32 [1]: shared gate_up tiles finished
+  size_t flags;      // uint64 [kFlagPlanes][largest one-launch grid]: hand-off flags of the one-launch layer
+  size_t rkeys;      // uint32 [kMaxUnits][E]: router logits of the one-launch layer as order-preserving
+                     // keys (0 = not yet written; the reader clears them after use)
+};
+
+// Workgroup roles of the one-launch small-M layer, in launch order: the
+// leader (workgroup 0: token preparation, top-k or the caller's ids, the
+// unit table and the routing flags), router rows (4 per workgroup, only when
+// the launch routes), shared gate_up (tile x K slice), routed gate_up
+// (unit x tile), shared down (tile x K slice), routed down (unit x tile).
+// S is the number of (token, slot) pairs, which bounds the distinct-expert
+// units.
+struct LayerGrid {
+  int gSG, gRG, gSD, gRD, grid;  // the router rows are workgroups 1 .. gSG-1
+};
+// Flag planes of the one-launch layer, one 64-bit flag per workgroup each.
+constexpr int kFlagPlanes = 4;  // routing, unit h ready, shared h ready, normalised tokens ready
+inline LayerGrid layer_roles(int H, int E, int I, int has_shared, int route, int S) {
+  const SharedSplit sg = shared_gu_split(H), sd = shared_dn_split(I);
+  LayerGrid g;
+  g.gSG = 1 + (route ? (E + 3) / 4 : 0);
+  g.gRG = g.gSG + (has_shared ? (I / 32) * sg.KS : 0);
+  g.gSD = g.gRG + S * (I / 32);
+  g.gRD = g.gSD + (has_shared ? (H / 64) * sd.KS : 0);
+  g.grid = g.gRD + S * (H / 64);
+  return g;
+}
+// The header is the same for every token count (a call of any M finds the
+// counters and flags where the previous call left them, all zero).
+inline size_t ws_header(int H, int E, int I, int has_shared, WsHeader* w) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
-  *err = take(4);
-  *route_cnt = take(4);
-  *shgu_cnt = take((size_t)4 * (I / 32));
-  *dn_cnt = take((size_t)4 * (H / 64));
+  const size_t cs = (size_t)4 * kCntStride;
+  w->err = take(4);
+  w->route_cnt = take(cs * kRouteCounters);
+  w->shgu_cnt = take(cs * (I / 32));
+  w->dn_cnt = take(cs * (H / 64));
+  w->hcnt = take(cs * kMaxUnits);
+  w->shdone = take(4);
+  w->flags = take((size_t)kFlagPlanes * 8 * layer_roles(H, E, I, has_shared, 1, kMaxUnits).grid);
+  w->rkeys = take((size_t)kMaxUnits * E * 4);
   return off;
 }
+
+// Row stride (floats) of the group corrections of h: whole 128-byte lines,
+// so that no line holds the values of two slots (they are produced by
+// different workgroups at different times and read through the scalar cache).
+#if defined(__HIPCC__)
+__host__ __device__
+#endif
+inline int hb_stride(int I) { return (I / 32 + 31) / 32 * 32; }
+
+// Workspace: counters and the sticky error word first, then the per-call
+// scratch arrays, each 256-byte aligned.
+struct WsLayout : WsHeader {
+  size_t logits;                             // fp32 [Mmax][E]
+  size_t h;                                  // bf16 [Mmax*k][I]
+  size_t h_sh;                               // bf16 [Mmax][I]
+  size_t shgu_part;                          // fp32 [Mmax][Tgu][KSgu][64]
+  size_t dpart;                              // fp32 [Mmax*k][H]
+  size_t shdn_part;                          // fp32 [Mmax][KSdn][H]
+  size_t ghist;                              // int32 [perm_groups(Mmax*k)][E] (moe_permute)
+  size_t gb;                                 // fp32 [Mmax][H/32] group corrections of the tokens
+  size_t hb;                                 // fp32 [Mmax*k][hb_stride(I)] group corrections of h
+  size_t total;
+  int Tgu, Tdn, KSgu, KSdn, CWgu, CWdn;
+};
 
 inline WsLayout ws_layout(int H, int E, int k, int I, int has_shared, int Mmax) {
   WsLayout w;
@@ -54,7 +117,7 @@ inline WsLayout ws_layout(int H, int E, int k, int I, int has_shared, int Mmax) 
   SharedSplit sd = shared_dn_split(I);
   w.KSgu = sg.KS; w.CWgu = sg.CW;
   w.KSdn = sd.KS; w.CWdn = sd.CW;
-  size_t off = ws_header(H, I, &w.err, &w.route_cnt, &w.shgu_cnt, &w.dn_cnt);
+  size_t off = ws_header(H, E, I, has_shared, &w);
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
   size_t M = (size_t)Mmax;
   w.logits = take(M * E * 4);
@@ -64,6 +127,8 @@ inline WsLayout ws_layout(int H, int E, int k, int I, int has_shared, int Mmax) 
   w.dpart = take(M * k * H * 4);
   w.shdn_part = take(has_shared ? M * w.KSdn * H * 4 : 0);
   w.ghist = take((size_t)perm_groups((long long)M * k) * E * 4);  // moe_permute
+  w.gb = take(M * (H / 32) * 4);
+  w.hb = take(M * k * hb_stride(I) * 4);
   w.total = off;
   return w;
 }
@@ -73,8 +138,7 @@ inline WsLayout ws_layout(int H, int E, int k, int I, int has_shared, int Mmax) 
 constexpr int kItemRows = 96;
 
 // Workspace of the many-token (prefill) path.
-struct PfLayout {
-  size_t err, route_cnt, shgu_cnt, dn_cnt;
+struct PfLayout : WsHeader {
   size_t logits;                    // fp32 [M][E]
   size_t rt_planes;                 // bf16 [3][E][H] router weights split in three exact parts
   size_t counts, offsets;           // int32 [E], [E+1]
@@ -91,7 +155,7 @@ struct PfLayout {
 
 inline PfLayout pf_layout(int H, int E, int k, int I, int has_shared, int M) {
   PfLayout w;
-  size_t off = ws_header(H, I, &w.err, &w.route_cnt, &w.shgu_cnt, &w.dn_cnt);
+  size_t off = ws_header(H, E, I, has_shared, &w);
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
   const size_t S = (size_t)M * k;
   // sum over experts of ceil(count / kItemRows) <= E + S / kItemRows
@@ -192,6 +256,10 @@ __device__ __forceinline__ void store_hilo(uint16_t* __restrict__ group_base, in
   group_base[32 + i] = lo;
 }
 
+// store_hilo through agent-coherent stores (read by other workgroups of the
+// same launch).
+__device__ __forceinline__ void store_hilo_coherent(uint16_t* __restrict__ group_base, int i, float v);
+
 // Eight bf16 weights (natural order) against 4 dwords of bf16 activations.
 __device__ __forceinline__ float dot_chunk_bf16(uint4 w, const uint32_t* xc, float acc) {
   acc = dot2_bf16(w.x, xc[0], acc);
@@ -222,6 +290,21 @@ __device__ __forceinline__ void st_coherent(float* p, float v) {
 __device__ __forceinline__ float ld_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void st_coherent(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t ld_coherent(const int32_t* p) {
+  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_coherent(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coherent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coherent(uint16_t* p, uint16_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Last-arriver protocol: each thread waits for its own coherent stores to
 // complete (s_waitcnt 0), the barrier gathers the workgroup, thread 0 counts
@@ -241,6 +324,17 @@ __device__ __forceinline__ bool arrive_last(int* counter, int expected, int* lds
   return *lds_flag != 0;
 }
 
+// arrive_last over n workgroups numbered i < n in groups of kArriveFan: each
+// group counts on cnt[(i / kArriveFan + 1) * kCntStride], the last of each
+// group on cnt[0].  A store completed before a workgroup's arrival is seen by
+// the last of all (each level's last arriver saw the arrivals below it).
+__device__ __forceinline__ bool arrive_last_tree(int* cnt, int i, int n, int* lds_flag) {
+  const int g = i / kArriveFan;
+  const int in_g = (n - g * kArriveFan) < kArriveFan ? (n - g * kArriveFan) : kArriveFan;
+  if (!arrive_last(&cnt[(g + 1) * kCntStride], in_g, lds_flag)) return false;
+  return arrive_last(cnt, (n + kArriveFan - 1) / kArriveFan, lds_flag);
+}
+
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses,
@@ -251,6 +345,50 @@ __device__ __forceinline__ void lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ void store_hilo_coherent(uint16_t* __restrict__ group_base, int i, float v) {
+  const uint16_t hi = f32_to_bf16(v);
+  const uint16_t lo = f32_to_bf16(v - bf16_to_f32(hi));
+  st_coherent(&group_base[i], hi);
+  st_coherent(&group_base[32 + i], lo);
+}
+
+// Hand-off flag inside one launch: thread 0 polls *f (agent-coherent) until it
+// is non-zero, then clears it for the next call (the flag belongs to this
+// workgroup alone); the workgroup then follows a full barrier (its acquire
+// fence keeps every later load of the workgroup after the poll).  Loads
+// after it that read the producer's data must be agent-coherent.  The
+// producer sets the flag only after its data stores have completed.  A wait
+// that gives up after kSpinLimit polls sets bit 1 of the error word.
+constexpr int kSpinLimit = 1 << 22;
+__device__ __forceinline__ uint64_t wait_flag(uint64_t* f, int32_t* err, uint64_t* lds_val) {
+  if (threadIdx.x == 0) {
+    int spins = 0;
+    uint64_t v;
+    while ((v = ld_coherent(f)) == 0) {
+      if (++spins > kSpinLimit) {
+        atomicOr(err, 2);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    st_coherent(f, (uint64_t)0);
+    *lds_val = v;
+  }
+  __syncthreads();
+  return *lds_val;
+}
+
+// A pointer passed through an empty asm after a wait: loads through it
+// (scalar loads from the constant address space in particular, which the
+// compiler may otherwise hoist) are issued after the wait.
+template <typename T>
+__device__ __forceinline__ T* after_wait(T* p) {
+  uint64_t v = reinterpret_cast<uint64_t>(p);
+  uint32_t lo = (uint32_t)uniform((int)(uint32_t)v), hi = (uint32_t)uniform((int)(v >> 32));
+  asm volatile("" : "+s"(lo), "+s"(hi));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
 }
 
 }  // namespace moe

@@ -35,6 +35,14 @@ hipError_t launch_down(const Shape& s, const uint8_t* packed, const PackedLayout
                        const int32_t* ids, const float* w, uint16_t* out, uint8_t* ws, const WsLayout& L,
                        hipStream_t st);
 
+// The whole small-M layer in one launch (M*k <= kMaxUnits): with route, the
+// router, top-k and softmax too (ids and w are written); without, ids and w
+// are read.  rmsnorm only with route.
+bool layer_supported(const Shape& s, int M);
+hipError_t launch_layer(const Shape& s, const uint8_t* packed, const PackedLayout& PL, const float* router_w,
+                        const uint16_t* x, int M, bool route, bool rmsnorm, float eps, uint16_t* x_norm,
+                        int32_t* ids, float* w, uint16_t* out, uint8_t* ws, const WsLayout& L, hipStream_t st);
+
 hipError_t launch_permute(const Shape& s, const int32_t* ids, int M, int32_t* counts, int32_t* offsets,
                           int32_t* perm, int32_t* ghist, int32_t* err, hipStream_t st);
 

@@ -1,0 +1,239 @@
+// route_dev.hpp — device code shared by the small-M router kernels: the
+// launch arguments and the per-token top-k selection with softmax weights.
+#pragma once
+#include "launch.hpp"
+
+namespace moe {
+
+struct RouteArgs {
+  int M, E, k, H;
+  int rmsnorm;
+  float eps;
+  const float* __restrict__ wr;
+  const uint16_t* __restrict__ x;
+  uint16_t* __restrict__ x_norm;
+  float* __restrict__ logits;  // [M][E]
+  int32_t* __restrict__ cnt;
+  int32_t* __restrict__ ids;
+  float* __restrict__ w;
+};
+
+// Order-preserving map of a float to an unsigned key (larger float, larger key).
+__device__ __forceinline__ uint32_t sort_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// k-th largest of one 32-bit key per lane (keys of absent lanes are 0),
+// found bit by bit from the top with one ballot per bit.
+__device__ __forceinline__ uint32_t kth_largest_lane_key(uint32_t key, int k) {
+  uint32_t thr = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    if (__popcll(__ballot(key >= cand)) >= k) thr = cand;
+  }
+  return thr;
+}
+
+// Top-k of logits[0..E) for one token, by one wavefront (E <= 512: lane l
+// holds experts l + 64*j as order-preserving keys).
+//  1. Prune: the k-th largest of the 64 lane maxima is at most the k-th
+//     largest logit (those k maxima are k distinct logits), so only logits
+//     at or above it can win; typically about k of them survive.
+//  2. If more than 64 survive (heavy ties), select exactly instead: the k-th
+//     largest key bit by bit over all keys, every key above it, and the
+//     lowest ids among the keys equal to it.
+//  3. The survivors are gathered into lanes 0..C-1 and ranked by
+//     (key desc, id asc); ranks 0..k-1 are the result, in that order.
+// The selection itself on keys held in registers (key[j] of expert
+// lane + 64*j; absent entries are not present).  Lanes < k return the id and
+// softmax weight of rank `lane`.
+constexpr int kTopkEPL = kMaxExperts / kWave;
+__device__ __forceinline__ void topk_select(const uint32_t (&key)[kTopkEPL], const bool (&present)[kTopkEPL], int k,
+                                            int lane, int* lds, int& out_id, float& out_w) {
+  constexpr int EPL = kTopkEPL;
+  uint32_t lmax = 0;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) lmax = (present[j] && key[j] > lmax) ? key[j] : lmax;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const uint32_t thr0 = kth_largest_lane_key(lmax, k);
+  uint32_t cand = 0;
+  int C = 0;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const bool c = present[j] && key[j] >= thr0;
+    cand |= (uint32_t)c << j;
+    C += __popcll(__ballot(c));
+  }
+  if (C > kWave) {
+    // exact selection of exactly k entries
+    uint32_t thr = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cb = thr | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) cnt += __popcll(__ballot(present[j] && key[j] >= cb));
+      if (cnt >= k) thr = cb;
+    }
+    int room = k;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) room -= __popcll(__ballot(present[j] && key[j] > thr));
+    cand = 0;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {  // ascending j, then lane: ascending id
+      const bool eq = present[j] && key[j] == thr;
+      const uint64_t eb = __ballot(eq);
+      const bool take = (present[j] && key[j] > thr) || (eq && __popcll(eb & lt) < room);
+      cand |= (uint32_t)take << j;
+      room -= __popcll(eb);
+      if (room < 0) room = 0;
+    }
+    C = k;
+  }
+  // gather the C candidates into lanes 0..C-1 (through LDS)
+  uint32_t* lkey = reinterpret_cast<uint32_t*>(lds);
+  int* lid = lds + kWave;
+  int* lorder = lds + 2 * kWave;
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const bool c = (cand >> j) & 1u;
+    const uint64_t bal = __ballot(c);
+    if (c) {
+      const int pos = base + __popcll(bal & lt);
+      lkey[pos] = key[j];
+      lid[pos] = lane + kWave * j;
+    }
+    base += __popcll(bal);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  const uint32_t mk = lane < C ? lkey[lane] : 0u;
+  const int mi = lane < C ? lid[lane] : 0x7FFFFFFF;
+  int rank = 0;
+  for (int c = 0; c < C; ++c) {
+    const uint32_t ok = (uint32_t)__builtin_amdgcn_readlane((int)mk, c);
+    const int oi = __builtin_amdgcn_readlane(mi, c);
+    rank += (ok > mk || (ok == mk && oi < mi)) ? 1 : 0;
+  }
+  if (lane < C && rank < k) lorder[rank] = lane;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  const int src = lane < k ? lorder[lane] : 0;
+  const uint32_t rk = __shfl(mk, src, 64);
+  const int ri = __shfl(mi, src, 64);
+  const float v = lane < k ? key_value(rk) : 0.f;
+  const float vmax = __shfl(v, 0, 64);
+  const float ex = lane < k ? expf(v - vmax) : 0.f;
+  const float sum = wave_sum(ex);
+  out_id = ri;
+  out_w = ex / sum;
+}
+
+// Top-k of logits[t][0..E) (fp32, agent-coherent: written by other
+// workgroups of the launch); stores ids and weights of token t.
+__device__ __forceinline__ void topk_token(const RouteArgs& a, int t, int lane, int* lds) {
+  uint32_t key[kTopkEPL];
+  bool present[kTopkEPL];
+#pragma unroll
+  for (int j = 0; j < kTopkEPL; ++j) {
+    const int e = lane + kWave * j;
+    present[j] = e < a.E;
+    key[j] = present[j] ? sort_key(ld_coherent(&a.logits[(size_t)t * a.E + e])) : 0u;
+  }
+  int id;
+  float w;
+  topk_select(key, present, a.k, lane, lds, id, w);
+  if (lane < a.k) {
+    st_coherent(&a.ids[(size_t)t * a.k + lane], id);
+    st_coherent(&a.w[(size_t)t * a.k + lane], w);
+  }
+}
+
+// The RMSNorm divisor of a token from its sum of squares (unit gain).
+__device__ __forceinline__ float rms_divisor(float ss, int H, float eps) { return sqrtf(ss / (float)H + eps); }
+
+// One wavefront's view of token t: lane l holds inputs 256*i + 4*l .. +3 as
+// float (raw, or RMS-normalised and rounded to bf16); `packed` receives the
+// same values as bf16 pairs.  The sum of squares runs in a fixed order
+// (i, then the 4 inputs, then the xor butterfly), so every wavefront that
+// calls this gets the same bits.
+template <int NI>
+__device__ __forceinline__ void load_token(const uint16_t* __restrict__ xt, int H, int lane, bool rmsnorm, float eps,
+                                           float (&xv)[NI][4], uint2 (&packed)[NI]) {
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const uint2 v = *reinterpret_cast<const uint2*>(xt + 256 * i + 4 * lane);
+    packed[i] = v;
+    xv[i][0] = __uint_as_float(v.x << 16);
+    xv[i][1] = __uint_as_float(v.x & 0xFFFF0000u);
+    xv[i][2] = __uint_as_float(v.y << 16);
+    xv[i][3] = __uint_as_float(v.y & 0xFFFF0000u);
+  }
+  if (!rmsnorm) return;
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ss = fmaf(xv[i][q], xv[i][q], ss);
+  ss = wave_sum(ss);
+  const float d = rms_divisor(ss, H, eps);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    uint16_t bq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      bq[q] = f32_to_bf16(xv[i][q] / d);
+      xv[i][q] = bf16_to_f32(bq[q]);
+    }
+    packed[i].x = (uint32_t)bq[0] | ((uint32_t)bq[1] << 16);
+    packed[i].y = (uint32_t)bq[2] | ((uint32_t)bq[3] << 16);
+  }
+}
+
+// Logits of router row e for every token (one wavefront, rows past E load
+// row E-1 and store nothing).  The row stays in registers while the
+// wavefront walks the tokens; `writer` also stores the normalised tokens.
+// With keys, each logit is stored as its order-preserving key (never 0)
+// instead of into a.logits.
+template <int NI>
+__device__ __forceinline__ void router_row(const RouteArgs& a, int e, int lane, bool writer, uint32_t* keys = nullptr) {
+  const bool has_row = e < a.E;
+  const int er = has_row ? e : a.E - 1;
+  float4 wr[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) wr[i] = *reinterpret_cast<const float4*>(a.wr + (size_t)er * a.H + 256 * i + 4 * lane);
+  for (int t = 0; t < a.M; ++t) {
+    float xv[NI][4];
+    uint2 packed[NI];
+    load_token<NI>(a.x + (size_t)t * a.H, a.H, lane, a.rmsnorm != 0, a.eps, xv, packed);
+    if (a.rmsnorm && writer) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        *reinterpret_cast<uint2*>(a.x_norm + (size_t)t * a.H + 256 * i + 4 * lane) = packed[i];
+    }
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      acc = fmaf(wr[i].x, xv[i][0], acc);
+      acc = fmaf(wr[i].y, xv[i][1], acc);
+      acc = fmaf(wr[i].z, xv[i][2], acc);
+      acc = fmaf(wr[i].w, xv[i][3], acc);
+    }
+    acc = wave_sum(acc);
+    if (has_row && lane == 0) {
+      if (keys) {
+        const uint32_t key = sort_key(acc);  // 0 only for one NaN pattern: stored as the lowest key instead
+        st_coherent(reinterpret_cast<int32_t*>(&keys[(size_t)t * a.E + e]), (int32_t)(key ? key : 1u));
+      }
+      else st_coherent(&a.logits[(size_t)t * a.E + e], acc);
+    }
+  }
+}
+
+}  // namespace moe
