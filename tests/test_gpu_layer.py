@@ -93,21 +93,26 @@ def test_layer_equals_route_then_forward(ling, M):
     assert torch.equal(out.view(torch.int16), r_out.view(torch.int16))
 
 
-def test_stages_equal_forward(ling):
-    """moe_gate_up_w4a16 + moe_down_w4a16 (two launches) give the bits of
-    moe_forward_w4a16 (one launch at small M): the same arithmetic in the same
-    order, only the hand-off differs."""
+def test_stages_match_oracle(ling, oracle_mod):
+    """moe_gate_up_w4a16 + moe_down_w4a16 (two launches, h kept as a bf16
+    pair) and moe_forward_w4a16 (one launch at small M, h of each tile in
+    scaled fp16) both against the oracle on the same ids and weights."""
     import torch
     from w4a16_grouped_quantized_amd import binding as B
     for M in (1, 4):
-        x_dev = to_dev_bf16(synth.make_tokens(synth.LING, 650 + M, M))
+        x = synth.make_tokens(synth.LING, 650 + M, M)
+        x_dev = to_dev_bf16(x)
         ids, w = ling.route(x_dev)
         out = ling.forward(x_dev, ids, w)
         out2 = torch.empty_like(out)
         B.gate_up(ling.cfg, ling.dev.packed, x_dev, ids, ling.ws.buf)
         B.down(ling.cfg, ling.dev.packed, ids, w, out2, ling.ws.buf)
         torch.cuda.synchronize()
-        assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), f"M={M}"
+        assert ling.device_error() == 0
+        ref, bad = oracle_mod.forward(synth.LING, ling.layer, x, ids.cpu().numpy(), w.cpu().numpy().astype(np.float64))
+        assert bad == 0
+        check_out(from_dev_bf16(out), ref, f"forward M={M}")
+        check_out(from_dev_bf16(out2), ref, f"stages M={M}")
 
 
 @pytest.mark.parametrize("shared", [False, True])

@@ -41,6 +41,9 @@ struct WsHeader {
   size_t dn_cnt;     // int32 [H/64] spaced: partial rows finished per down tile
   size_t hcnt;       // int32 [kMaxUnits] spaced: gate_up tiles finished per routed unit
   size_t shdone;     // int32 [1]: shared gate_up tiles finished
+  size_t udone;      // int32 [1]: routed units finished (one-launch layer)
+  size_t sdone;      // int32 [1]: shared down workgroups finished (one-launch layer)
+  size_t cdone;      // int32 [1]: combine workgroups finished (one-launch layer)
   size_t flags;      // uint64 [kFlagPlanes][largest one-launch grid]: hand-off flags of the one-launch layer
   size_t rkeys;      // uint32 [kMaxUnits][E]: router logits of the one-launch layer as order-preserving
                      // keys (0 = not yet written; the reader clears them after use)
@@ -49,23 +52,26 @@ struct WsHeader {
 // Workgroup roles of the one-launch small-M layer, in launch order: the
 // leader (workgroup 0: token preparation, top-k or the caller's ids, the
 // unit table and the routing flags), router rows (4 per workgroup, only when
-// the launch routes), shared gate_up (tile x K slice), routed gate_up
-// (unit x tile), shared down (tile x K slice), routed down (unit x tile).
-// S is the number of (token, slot) pairs, which bounds the distinct-expert
-// units.
+// the launch routes), shared gate_up (tile x K slice), routed experts
+// (unit x gate_up tile, each also applying its slice of the down matrix),
+// shared down (tile x K slice), combine (token x output tile x split).  S = M*k
+// (token, slot) pairs bound the distinct-expert units.
 struct LayerGrid {
-  int gSG, gRG, gSD, gRD, grid;  // the router rows are workgroups 1 .. gSG-1
+  int gSG, gRG, gSD, gCB, grid;  // the router rows are workgroups 1 .. gSG-1
 };
+// Combine workgroups per (token, 64-row output tile): each sums 64 /
+// kCombineSplit output rows, so that the partial rows are read by many CUs.
+constexpr int kCombineSplit = 4;
 // Flag planes of the one-launch layer, one 64-bit flag per workgroup each.
-constexpr int kFlagPlanes = 4;  // routing, unit h ready, shared h ready, normalised tokens ready
-inline LayerGrid layer_roles(int H, int E, int I, int has_shared, int route, int S) {
+constexpr int kFlagPlanes = 3;  // routing, shared h ready, normalised tokens ready
+inline LayerGrid layer_roles(int H, int E, int I, int has_shared, int route, int M, int k) {
   const SharedSplit sg = shared_gu_split(H), sd = shared_dn_split(I);
   LayerGrid g;
   g.gSG = 1 + (route ? (E + 3) / 4 : 0);
   g.gRG = g.gSG + (has_shared ? (I / 32) * sg.KS : 0);
-  g.gSD = g.gRG + S * (I / 32);
-  g.gRD = g.gSD + (has_shared ? (H / 64) * sd.KS : 0);
-  g.grid = g.gRD + S * (H / 64);
+  g.gSD = g.gRG + M * k * (I / 32);
+  g.gCB = g.gSD + (has_shared ? (H / 64) * sd.KS : 0);
+  g.grid = g.gCB + M * (H / 64) * kCombineSplit;
   return g;
 }
 // The header is the same for every token count (a call of any M finds the
@@ -79,19 +85,16 @@ inline size_t ws_header(int H, int E, int I, int has_shared, WsHeader* w) {
   w->shgu_cnt = take(cs * (I / 32));
   w->dn_cnt = take(cs * (H / 64));
   w->hcnt = take(cs * kMaxUnits);
-  w->shdone = take(4);
-  w->flags = take((size_t)kFlagPlanes * 8 * layer_roles(H, E, I, has_shared, 1, kMaxUnits).grid);
+  w->shdone = take(cs);
+  w->udone = take(cs);
+  w->sdone = take(cs);
+  w->cdone = take(cs);
+  // the largest grid: M*k and M both at kMaxUnits (k = 1)
+  w->flags = take((size_t)kFlagPlanes * 8 * layer_roles(H, E, I, has_shared, 1, kMaxUnits, 1).grid);
   w->rkeys = take((size_t)kMaxUnits * E * 4);
   return off;
 }
 
-// Row stride (floats) of the group corrections of h: whole 128-byte lines,
-// so that no line holds the values of two slots (they are produced by
-// different workgroups at different times and read through the scalar cache).
-#if defined(__HIPCC__)
-__host__ __device__
-#endif
-inline int hb_stride(int I) { return (I / 32 + 31) / 32 * 32; }
 
 // Workspace: counters and the sticky error word first, then the per-call
 // scratch arrays, each 256-byte aligned.
@@ -103,8 +106,8 @@ struct WsLayout : WsHeader {
   size_t dpart;                              // fp32 [Mmax*k][H]
   size_t shdn_part;                          // fp32 [Mmax][KSdn][H]
   size_t ghist;                              // int32 [perm_groups(Mmax*k)][E] (moe_permute)
+  size_t ypart;                              // fp32 [H/64][Mmax*k][I/32][64] down partials (one-launch layer)
   size_t gb;                                 // fp32 [Mmax][H/32] group corrections of the tokens
-  size_t hb;                                 // fp32 [Mmax*k][hb_stride(I)] group corrections of h
   size_t total;
   int Tgu, Tdn, KSgu, KSdn, CWgu, CWdn;
 };
@@ -127,8 +130,9 @@ inline WsLayout ws_layout(int H, int E, int k, int I, int has_shared, int Mmax) 
   w.dpart = take(M * k * H * 4);
   w.shdn_part = take(has_shared ? M * w.KSdn * H * 4 : 0);
   w.ghist = take((size_t)perm_groups((long long)M * k) * E * 4);  // moe_permute
+  const size_t S1 = M * k < (size_t)kMaxUnits ? M * k : (size_t)kMaxUnits;  // one-launch calls only
+  w.ypart = take(S1 * (I / 32) * H * 4);
   w.gb = take(M * (H / 32) * 4);
-  w.hb = take(M * k * hb_stride(I) * 4);
   w.total = off;
   return w;
 }
@@ -183,6 +187,7 @@ inline PfLayout pf_layout(int H, int E, int k, int I, int has_shared, int M) {
 // ---------------------------------------------------------------- device helpers
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 half2_t;
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
@@ -281,15 +286,26 @@ __device__ __forceinline__ float wave_sum(float v) {
 // XCDs, whose L2 caches are not coherent with each other, and an agent-scope
 // release fence (a full L2 write-back) per workgroup costs several
 // microseconds per launch on this part.  So the data itself travels with
-// agent-coherent accesses: stores write through to the coherent level, loads
-// read from it, and the only ordering needed is that a producer's stores have
-// completed before its arrival is counted.
+// agent-coherent stores (written through to the coherent level), and the
+// only ordering needed is that a producer's stores have completed before its
+// arrival or flag is seen.  Agent-coherent loads are served one at a time
+// per wavefront (about 0.1 us each even on an idle part), so they are kept
+// for polls; data is read with ld_fresh (below).
 __device__ __forceinline__ void st_coherent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float ld_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// A plain load of data stored agent-coherently by other workgroups of this
+// launch, issued after the hand-off that publishes it (behind a barrier with
+// an acquire fence).  Correct because the reader's caches cannot hold an
+// older copy: they start each launch invalidated, the reader touches the
+// line for the first time here, and every byte of a line read this way was
+// written before its hand-off.  Unlike ld_coherent it pipelines.
+template <typename T>
+__device__ __forceinline__ T ld_fresh(const T* p) { return *p; }
+
 __device__ __forceinline__ void st_coherent(int32_t* p, int32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -310,7 +326,8 @@ __device__ __forceinline__ void st_coherent(uint16_t* p, uint16_t v) {
 // complete (s_waitcnt 0), the barrier gathers the workgroup, thread 0 counts
 // the arrival.  The workgroup that arrives last sees every other
 // workgroup's coherent stores, resets the counter for the next call and gets
-// true in all its threads.  Loads that follow must be ld_coherent.
+// true in all its threads.  Loads that follow read the others' data with
+// ld_fresh.
 __device__ __forceinline__ bool arrive_last(int* counter, int expected, int* lds_flag) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();

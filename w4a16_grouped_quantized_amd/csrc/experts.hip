@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(const ExpArgs a) {
       float pv[kMaxKSplit];
 #pragma unroll
       for (int s2 = 0; s2 < kMaxKSplit; ++s2)
-        pv[s2] = s2 < a.KSgu ? ld_coherent(&a.shgu_part[(((size_t)t * a.Tgu + b) * a.KSgu + s2) * kWave + lane]) : 0.f;
+        pv[s2] = s2 < a.KSgu ? ld_fresh(&a.shgu_part[(((size_t)t * a.Tgu + b) * a.KSgu + s2) * kWave + lane]) : 0.f;
       float part = 0.f;
 #pragma unroll
       for (int s2 = 0; s2 < kMaxKSplit; ++s2) part += pv[s2];

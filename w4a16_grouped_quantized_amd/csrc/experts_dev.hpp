@@ -296,9 +296,8 @@ __device__ __forceinline__ float group_bias_lds(const uint32_t* act, int g) {
 // rows n of tile b, in slot order then slice order, rounded to bf16.  The
 // routed partials arrive already multiplied by their slot's weight.  With
 // check_ids, slots whose id is out of range add nothing (their partial was
-// never written) and are recorded in the error word; ids are read
-// agent-coherently.  All loads of a block of 8 slots are issued before any of
-// them is used.
+// never written) and are recorded in the error word.  All loads of a block
+// of 8 slots are issued before any of them is used.
 __device__ void combine_tile(const ExpArgs& a, int b, bool check_ids) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = 64 * b + lane;
@@ -312,8 +311,8 @@ __device__ void combine_tile(const ExpArgs& a, int b, bool check_ids) {
       for (int jj = 0; jj < 8; ++jj) {
         const int p = t * a.k + j0 + jj;
         const bool in = j0 + jj < a.k;
-        ev[jj] = (in && check_ids) ? ld_coherent(&a.ids[p]) : 0;
-        pv[jj] = in ? ld_coherent(&a.dpart[(size_t)p * a.H + n]) : 0.f;
+        ev[jj] = (in && check_ids) ? a.ids[p] : 0;
+        pv[jj] = in ? ld_fresh(&a.dpart[(size_t)p * a.H + n]) : 0.f;
       }
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
@@ -326,7 +325,7 @@ __device__ void combine_tile(const ExpArgs& a, int b, bool check_ids) {
       float sv[kMaxKSplit];
 #pragma unroll
       for (int s2 = 0; s2 < kMaxKSplit; ++s2)
-        sv[s2] = s2 < a.KSdn ? ld_coherent(&a.shdn_part[((size_t)t * a.KSdn + s2) * a.H + n]) : 0.f;
+        sv[s2] = s2 < a.KSdn ? ld_fresh(&a.shdn_part[((size_t)t * a.KSdn + s2) * a.H + n]) : 0.f;
 #pragma unroll
       for (int s2 = 0; s2 < kMaxKSplit; ++s2) y += sv[s2];
     }

@@ -135,8 +135,8 @@ __device__ __forceinline__ void topk_select(const uint32_t (&key)[kTopkEPL], con
   out_w = ex / sum;
 }
 
-// Top-k of logits[t][0..E) (fp32, agent-coherent: written by other
-// workgroups of the launch); stores ids and weights of token t.
+// Top-k of logits[t][0..E) (fp32, written by the other workgroups of the
+// launch before their arrival); stores ids and weights of token t.
 __device__ __forceinline__ void topk_token(const RouteArgs& a, int t, int lane, int* lds) {
   uint32_t key[kTopkEPL];
   bool present[kTopkEPL];
@@ -144,7 +144,7 @@ __device__ __forceinline__ void topk_token(const RouteArgs& a, int t, int lane, 
   for (int j = 0; j < kTopkEPL; ++j) {
     const int e = lane + kWave * j;
     present[j] = e < a.E;
-    key[j] = present[j] ? sort_key(ld_coherent(&a.logits[(size_t)t * a.E + e])) : 0u;
+    key[j] = present[j] ? sort_key(ld_fresh(&a.logits[(size_t)t * a.E + e])) : 0u;
   }
   int id;
   float w;
