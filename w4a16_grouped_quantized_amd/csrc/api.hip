@@ -264,7 +264,7 @@ const char* moe_build_info(void) {
          "route=wave-per-row-fp32+lastwg-topk|mfma-bf16x3(M>=33) "
          "gate_up=int4-dot2bf16-sgpr-act(GW20P4|GW2P2)+shared-bf16(KS-split,lastwg) "
          "down=int4-dot2bf16(GW6P2|GW1P1)+lastwg-combine "
-         "layer(M*k<=64)=one-launch(router+topk+shared+routed gate_up/down+combine, flag hand-offs) "
+         "layer(M*k<=64)=one-launch(router, shared, routed gate_up, down+combine; tagged hand-offs) "
          "prefill(M*k>=513)=grouped-mfma-f16-exact-int4(96-row items,xcd-aware)+shared-mfma-bf16 "
          "permute=multi-wg-stable-counting-sort "
          "max_experts=512 max_decode_slots=4096";

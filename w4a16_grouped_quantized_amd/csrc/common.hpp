@@ -24,77 +24,80 @@ constexpr int kCntStride = 64;
 // Last-arriver trees: groups of kArriveFan workgroups count on their own
 // counter, the last of each group on a top counter.
 constexpr int kArriveFan = 16;
-// Distinct-expert units of the one-launch small-M layer (M*k <= this).
+// (token, slot) pairs of the one-launch small-M layer (M*k <= this).
 constexpr int kMaxUnits = 64;
+// Router keys one launch of that layer can hold (M*E <= this).
+constexpr int kMaxLayerKeys = 8192;
+// Counters its workgroups arrive on (workgroup b on b % this), so that the
+// arrivals of one call spread over several lines.
+constexpr int kArriveCounters = 8;
 // Router workgroups (4 rows each) of up to 512 experts: one top counter and
 // one per group of kArriveFan.
 constexpr int kRouteCounters = 1 + (512 / 4 + kArriveFan - 1) / kArriveFan;
 
-// Both paths share one header: the error word at offset 0 and the small-M
+// Workgroup roles of the one-launch small-M layer, in launch order: the
+// leader (workgroup 0: the call's tag, the normalised tokens), router rows
+// (4 per workgroup, only when the launch routes), shared gate_up (tile x K
+// slice), routed gate_up (slot x gate_up tile; slots past the number of
+// distinct experts have nothing to do), down (kDnRows output rows each:
+// every routed and the shared down projection of those rows, and the
+// output).  S = M*k (token, slot) pairs bound the distinct-expert units.
+struct LayerGrid {
+  int gSG, gGU, gDN, grid;  // the router rows are workgroups 1 .. gSG-1
+};
+constexpr int kDnRows = 8;
+inline LayerGrid layer_roles(int H, int E, int I, int has_shared, int route, int M, int k) {
+  const SharedSplit sg = shared_gu_split(H);
+  LayerGrid g;
+  g.gSG = 1 + (route ? (E + 3) / 4 : 0);
+  g.gGU = g.gSG + (has_shared ? (I / 32) * sg.KS : 0);
+  g.gDN = g.gGU + M * k * (I / 32);
+  g.grid = g.gDN + H / kDnRows;
+  return g;
+}
+
+// Both paths share one header: the error word at offset 0, the small-M
 // path's arrival counters, which must stay zero between calls whichever
-// path ran last (each counter is reset by the workgroup that completes it).
-// Per-call arrays follow the header.
+// path ran last (each counter is reset by the workgroup that completes it),
+// and the hand-off words of the one-launch layer.  Those carry the call's
+// tag (a 32-bit count of one-launch calls on this workspace, never 0) in
+// their high word, so a reader tells this call's data from anything older
+// without the words ever being cleared.  Per-call arrays follow the header.
 struct WsHeader {
   size_t err;        // int32 sticky error word
   size_t route_cnt;  // int32 [kRouteCounters] spaced: top counter, then one per group
   size_t shgu_cnt;   // int32 [I/32] spaced: K slices finished per shared gate_up tile
   size_t dn_cnt;     // int32 [H/64] spaced: partial rows finished per down tile
-  size_t hcnt;       // int32 [kMaxUnits] spaced: gate_up tiles finished per routed unit
-  size_t shdone;     // int32 [1]: shared gate_up tiles finished
-  size_t udone;      // int32 [1]: routed units finished (one-launch layer)
-  size_t sdone;      // int32 [1]: shared down workgroups finished (one-launch layer)
-  size_t cdone;      // int32 [1]: combine workgroups finished (one-launch layer)
-  size_t flags;      // uint64 [kFlagPlanes][largest one-launch grid]: hand-off flags of the one-launch layer
-  size_t rkeys;      // uint32 [kMaxUnits][E]: router logits of the one-launch layer as order-preserving
-                     // keys (0 = not yet written; the reader clears them after use)
+  size_t epoch;      // uint32: tag of the last one-launch call
+  size_t arrive;     // int32 [kArriveCounters] spaced: workgroups that have read the epoch this call
+  size_t flags;      // uint64 [largest one-launch grid]: normalised tokens ready, per workgroup (cleared by it)
+  size_t rkeys;      // uint64 [kMaxLayerKeys]: router logits [M][E] as order-preserving keys | tag
+  size_t hval;       // uint64 [kMaxUnits][I/32][16]: h per (slot, tile) as fp16 pairs | tag
+  size_t hmeta;      // uint64 [kMaxUnits][I/32]: the power-of-two exponent of that h | tag
+  size_t hsh;        // uint64 [kMaxUnits][I]: shared-expert h per token, fp32 bits | tag
 };
 
-// Workgroup roles of the one-launch small-M layer, in launch order: the
-// leader (workgroup 0: token preparation, top-k or the caller's ids, the
-// unit table and the routing flags), router rows (4 per workgroup, only when
-// the launch routes), shared gate_up (tile x K slice), routed experts
-// (unit x gate_up tile, each also applying its slice of the down matrix),
-// shared down (tile x K slice), combine (token x output tile x split).  S = M*k
-// (token, slot) pairs bound the distinct-expert units.
-struct LayerGrid {
-  int gSG, gRG, gSD, gCB, grid;  // the router rows are workgroups 1 .. gSG-1
-};
-// Combine workgroups per (token, 64-row output tile): each sums 64 /
-// kCombineSplit output rows, so that the partial rows are read by many CUs.
-constexpr int kCombineSplit = 4;
-// Flag planes of the one-launch layer, one 64-bit flag per workgroup each.
-constexpr int kFlagPlanes = 3;  // routing, shared h ready, normalised tokens ready
-inline LayerGrid layer_roles(int H, int E, int I, int has_shared, int route, int M, int k) {
-  const SharedSplit sg = shared_gu_split(H), sd = shared_dn_split(I);
-  LayerGrid g;
-  g.gSG = 1 + (route ? (E + 3) / 4 : 0);
-  g.gRG = g.gSG + (has_shared ? (I / 32) * sg.KS : 0);
-  g.gSD = g.gRG + M * k * (I / 32);
-  g.gCB = g.gSD + (has_shared ? (H / 64) * sd.KS : 0);
-  g.grid = g.gCB + M * (H / 64) * kCombineSplit;
-  return g;
-}
 // The header is the same for every token count (a call of any M finds the
-// counters and flags where the previous call left them, all zero).
+// counters and hand-off words where the previous call left them).
 inline size_t ws_header(int H, int E, int I, int has_shared, WsHeader* w) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
   const size_t cs = (size_t)4 * kCntStride;
+  (void)E;
   w->err = take(4);
   w->route_cnt = take(cs * kRouteCounters);
   w->shgu_cnt = take(cs * (I / 32));
   w->dn_cnt = take(cs * (H / 64));
-  w->hcnt = take(cs * kMaxUnits);
-  w->shdone = take(cs);
-  w->udone = take(cs);
-  w->sdone = take(cs);
-  w->cdone = take(cs);
+  w->epoch = take(4);
+  w->arrive = take(cs * kArriveCounters);
   // the largest grid: M*k and M both at kMaxUnits (k = 1)
-  w->flags = take((size_t)kFlagPlanes * 8 * layer_roles(H, E, I, has_shared, 1, kMaxUnits, 1).grid);
-  w->rkeys = take((size_t)kMaxUnits * E * 4);
+  w->flags = take((size_t)8 * layer_roles(H, E, I, has_shared, 1, kMaxUnits, 1).grid);
+  w->rkeys = take((size_t)kMaxLayerKeys * 8);
+  w->hval = take((size_t)kMaxUnits * (I / 32) * 16 * 8);
+  w->hmeta = take((size_t)kMaxUnits * (I / 32) * 8);
+  w->hsh = take(has_shared ? (size_t)kMaxUnits * I * 8 : 0);
   return off;
 }
-
 
 // Workspace: counters and the sticky error word first, then the per-call
 // scratch arrays, each 256-byte aligned.
@@ -106,8 +109,6 @@ struct WsLayout : WsHeader {
   size_t dpart;                              // fp32 [Mmax*k][H]
   size_t shdn_part;                          // fp32 [Mmax][KSdn][H]
   size_t ghist;                              // int32 [perm_groups(Mmax*k)][E] (moe_permute)
-  size_t ypart;                              // fp32 [H/64][Mmax*k][I/32][64] down partials (one-launch layer)
-  size_t gb;                                 // fp32 [Mmax][H/32] group corrections of the tokens
   size_t total;
   int Tgu, Tdn, KSgu, KSdn, CWgu, CWdn;
 };
@@ -130,9 +131,6 @@ inline WsLayout ws_layout(int H, int E, int k, int I, int has_shared, int Mmax) 
   w.dpart = take(M * k * H * 4);
   w.shdn_part = take(has_shared ? M * w.KSdn * H * 4 : 0);
   w.ghist = take((size_t)perm_groups((long long)M * k) * E * 4);  // moe_permute
-  const size_t S1 = M * k < (size_t)kMaxUnits ? M * k : (size_t)kMaxUnits;  // one-launch calls only
-  w.ypart = take(S1 * (I / 32) * H * 4);
-  w.gb = take(M * (H / 32) * 4);
   w.total = off;
   return w;
 }
@@ -214,6 +212,13 @@ __device__ __forceinline__ cptr32 as_scalar_ptr(const void* p) { return (cptr32)
 __device__ __forceinline__ uint32_t bf16_pair_magic() {
   uint32_t m;
   asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(m));
+  return m;
+}
+// fp16 (1024, 1024) likewise: (w & 0x000F000F) | magic is the fp16 pair
+// (1024 + u0, 1024 + u1), exact.
+__device__ __forceinline__ uint32_t fp16_pair_magic() {
+  uint32_t m;
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(m));
   return m;
 }
 

@@ -27,13 +27,19 @@ __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// k-th largest of one 32-bit key per lane (keys of absent lanes are 0),
-// found bit by bit from the top with one ballot per bit.
-__device__ __forceinline__ uint32_t kth_largest_lane_key(uint32_t key, int k) {
+// The largest value with zero low 16 bits that at least k lanes' keys reach
+// (keys of absent lanes are 0): a lower bound of the k-th largest key, within
+// its 16-bit prefix.  Two bits per step: the three candidate values of a step
+// are counted with independent ballots.
+__device__ __forceinline__ uint32_t kth_largest_lane_prefix(uint32_t key, int k) {
   uint32_t thr = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = thr | (1u << bit);
-    if (__popcll(__ballot(key >= cand)) >= k) thr = cand;
+#pragma unroll
+  for (int b = 30; b >= 16; b -= 2) {
+    const uint32_t c1 = thr | (1u << b), c2 = thr | (2u << b), c3 = thr | (3u << b);
+    const int n1 = __popcll(__ballot(key >= c1));
+    const int n2 = __popcll(__ballot(key >= c2));
+    const int n3 = __popcll(__ballot(key >= c3));
+    thr = n3 >= k ? c3 : n2 >= k ? c2 : n1 >= k ? c1 : thr;
   }
   return thr;
 }
@@ -42,12 +48,15 @@ __device__ __forceinline__ uint32_t kth_largest_lane_key(uint32_t key, int k) {
 // holds experts l + 64*j as order-preserving keys).
 //  1. Prune: the k-th largest of the 64 lane maxima is at most the k-th
 //     largest logit (those k maxima are k distinct logits), so only logits
-//     at or above it can win; typically about k of them survive.
+//     at or above it can win.  The bound used is that value with its low 16
+//     bits cleared; typically about k logits survive.
 //  2. If more than 64 survive (heavy ties), select exactly instead: the k-th
 //     largest key bit by bit over all keys, every key above it, and the
 //     lowest ids among the keys equal to it.
-//  3. The survivors are gathered into lanes 0..C-1 and ranked by
-//     (key desc, id asc); ranks 0..k-1 are the result, in that order.
+//  3. The survivors are gathered into LDS slots 0..C-1; lane c < C ranks
+//     survivor c by (key desc, id asc) against all of them (read four at a
+//     time at wavefront-uniform addresses); ranks 0..k-1 are the result, in
+//     that order.
 // The selection itself on keys held in registers (key[j] of expert
 // lane + 64*j; absent entries are not present).  Lanes < k return the id and
 // softmax weight of rank `lane`.
@@ -59,7 +68,7 @@ __device__ __forceinline__ void topk_select(const uint32_t (&key)[kTopkEPL], con
 #pragma unroll
   for (int j = 0; j < EPL; ++j) lmax = (present[j] && key[j] > lmax) ? key[j] : lmax;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const uint32_t thr0 = kth_largest_lane_key(lmax, k);
+  const uint32_t thr0 = kth_largest_lane_prefix(lmax, k);
   uint32_t cand = 0;
   int C = 0;
 #pragma unroll
@@ -93,7 +102,7 @@ __device__ __forceinline__ void topk_select(const uint32_t (&key)[kTopkEPL], con
     }
     C = k;
   }
-  // gather the C candidates into lanes 0..C-1 (through LDS)
+  // gather the C candidates into LDS slots 0..C-1
   uint32_t* lkey = reinterpret_cast<uint32_t*>(lds);
   int* lid = lds + kWave;
   int* lorder = lds + 2 * kWave;
@@ -115,22 +124,32 @@ __device__ __forceinline__ void topk_select(const uint32_t (&key)[kTopkEPL], con
   const uint32_t mk = lane < C ? lkey[lane] : 0u;
   const int mi = lane < C ? lid[lane] : 0x7FFFFFFF;
   int rank = 0;
-  for (int c = 0; c < C; ++c) {
-    const uint32_t ok = (uint32_t)__builtin_amdgcn_readlane((int)mk, c);
-    const int oi = __builtin_amdgcn_readlane(mi, c);
-    rank += (ok > mk || (ok == mk && oi < mi)) ? 1 : 0;
+  for (int c0 = 0; c0 < C; c0 += 4) {
+    const uint4 k4 = *reinterpret_cast<const uint4*>(lkey + c0);
+    const int4 i4 = *reinterpret_cast<const int4*>(lid + c0);
+    const uint32_t ok[4] = {k4.x, k4.y, k4.z, k4.w};
+    const int oi[4] = {i4.x, i4.y, i4.z, i4.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      rank += (c0 + q < C && (ok[q] > mk || (ok[q] == mk && oi[q] < mi))) ? 1 : 0;
   }
   if (lane < C && rank < k) lorder[rank] = lane;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
   const int src = lane < k ? lorder[lane] : 0;
-  const uint32_t rk = __shfl(mk, src, 64);
-  const int ri = __shfl(mi, src, 64);
+  const uint32_t rk = lkey[src];
+  const int ri = lid[src];
   const float v = lane < k ? key_value(rk) : 0.f;
-  const float vmax = __shfl(v, 0, 64);
+  const float vmax = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 0));
   const float ex = lane < k ? expf(v - vmax) : 0.f;
-  const float sum = wave_sum(ex);
+  float sum = ex;
+  if (k <= 8) {  // lanes 0..7 hold the k terms
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) sum += __shfl_xor(sum, off, 64);
+  } else {
+    sum = wave_sum(ex);
+  }
   out_id = ri;
   out_w = ex / sum;
 }
