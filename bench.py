@@ -230,10 +230,14 @@ def main():
                 "achieved": round(tflops, 2), "peak": 2500.0, "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4),
                 "traffic": None, "flops_per_launch": flops}
     else:
-        # Per-stage kernel durations: for each stage (route, gate_up, down) a
-        # graph of n back-to-back launches of that stage alone over the same
-        # rotation of layer copies, replayed between HIP events on the launch
-        # stream; duration per launch = elapsed / n.
+        # Per-entry-point durations, each a graph of n back-to-back launches of
+        # that call alone over the same rotation of layer copies, replayed
+        # between HIP events on the launch stream; duration per launch =
+        # elapsed / n.  route = moe_route (k_route), forward = moe_forward_w4a16
+        # on the routed ids (k_layer without routing at this size), and the
+        # two stage kernels of the separate-call API.
+        stage_names = ("route", "forward", "gate_up", "down")
+
         def stage_graph(stage, n):
             gs = torch.cuda.CUDAGraph()
             with torch.cuda.graph(gs):
@@ -244,14 +248,16 @@ def main():
                     if stage == 0:
                         B.route(cfg, rt, x_in, ids[j], w[j], ws.buf)
                     elif stage == 1:
+                        B.forward(cfg, pk, x_in, ids[j], w[j], out2[j], ws.buf)
+                    elif stage == 2:
                         B.gate_up(cfg, pk, x_in, ids[j], ws.buf)
                     else:
-                        B.down(cfg, pk, ids[j], w[j], out[j], ws.buf)
+                        B.down(cfg, pk, ids[j], w[j], out2[j], ws.buf)
             return gs
 
         def time_stages(n):
             res = []
-            for stage in range(3):
+            for stage in range(len(stage_names)):
                 gs = stage_graph(stage, n)
                 gs.replay()
                 torch.cuda.synchronize()
@@ -265,19 +271,29 @@ def main():
                 torch.cuda.synchronize()
                 res.append(e0.elapsed_time(e1) * 1e3 / (reps_s * n))
                 del gs
-            r = np.array(res)
-            return r, r
+            return np.array(res)
 
-        st_med, st_mean = time_stages(max(chunk, args.stage_steps))
-        log(f"stage us per launch (graph of back-to-back launches): route {st_mean[0]:.2f} "
-            f"gate_up {st_mean[1]:.2f} down {st_mean[2]:.2f}")
-        gu_bytes = (uniq if args.workload != "stack" else 8) * EXPERT_GU_BYTES + SHARED_GU_BYTES + M * 2560 * 2
-        achieved = gu_bytes / (st_mean[1] * 1e-6) / 1e9
-        stage = {"route": round(float(st_mean[0]), 3), "gate_up": round(float(st_mean[1]), 3),
-                 "down_combine": round(float(st_mean[2]), 3)}
-        roof = {"bound": "hbm", "kernel": "k_gate_up (routed int4 gate_up + SiLU, shared bf16 gate_up)",
-                "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None, "bytes_per_launch": int(gu_bytes)}
+        st = time_stages(max(chunk, args.stage_steps))
+        log("entry point us per launch (graph of back-to-back launches): " +
+            " ".join(f"{nm} {v:.2f}" for nm, v in zip(stage_names, st)))
+        stage = {nm: round(float(v), 3) for nm, v in zip(stage_names, st)}
+        n_uniq = uniq if args.workload != "stack" else 8
+        if args.path == "layer":
+            # the dominant kernel is the only one: k_layer, one launch per
+            # layer; its duration per launch is the timed region / launches
+            launches = n_layers if args.workload == "stack" else 1
+            us_launch = ms_per_step * 1e3 / launches
+            bytes_launch = bytes_per_step / launches
+            kernel = "k_layer (one launch per layer: router, top-k, shared and routed experts, output)"
+        else:
+            # separate calls: the dominant kernel is moe_forward_w4a16's k_layer
+            us_launch = float(st[1])
+            bytes_launch = step_bytes(int(round(n_uniq)), M) - ROUTER_BYTES
+            kernel = "k_layer without routing (moe_forward_w4a16: shared and routed experts, output)"
+        achieved = bytes_launch / (us_launch * 1e-6) / 1e9
+        roof = {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                "bytes_per_launch": int(bytes_launch), "us_per_launch": round(us_launch, 3)}
 
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib << 20
@@ -290,7 +306,7 @@ def main():
         log(f"calibration copy: {args.calib_copy_mib} MiB x 2")
 
     if roof.get("traffic") is None:
-        roof["traffic"] = measured_traffic(WORKLOAD_NAMES[args.workload])
+        roof["traffic"] = measured_traffic(WORKLOAD_NAMES[args.workload]) if args.path == "layer" or prefill else None
 
     cpu = None
     if not args.no_cpu_baseline:

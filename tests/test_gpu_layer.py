@@ -137,7 +137,7 @@ def test_layer_rmsnorm(ling, oracle_mod, M):
     r_ids, r_w = ling.route(y_dev, flags=B.MOE_F_INPUT_RMSNORM, x_norm=xn2)
     r_out = ling.forward(xn2, r_ids, r_w)
     torch.cuda.synchronize()
-    assert ling.device_error() == 0
+    assert ling.device_error() == 0, f"device error word {ling.device_error()}"
     assert torch.equal(xn.view(torch.int16), xn2.view(torch.int16))
     assert torch.equal(ids, r_ids) and torch.equal(w, r_w)
     assert torch.equal(out.view(torch.int16), r_out.view(torch.int16))
