@@ -129,13 +129,20 @@ int moe_forward_w4a16(const moe_config* cfg /* host */, const void* packed, cons
                       int32_t M, const int32_t* topk_ids, const float* topk_w, uint16_t* out,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* flag for moe_layer_w4a16 */
+#define MOE_F_ONE_LAUNCH 0x2u  /* use the one-launch kernel for every M it supports
+                                  (M*top_k <= 64), not only for M = 1 */
+
 /* One whole layer for a step of M tokens: moe_route followed by
- * moe_forward_w4a16 on the ids and weights it produced, with the same
- * results (topk_ids, topk_w, x_norm and out are all written).  For small M
- * (M*top_k <= 64, the decode and verify steps) the router, the top-k and the
- * expert FFNs run as one launch whose routed weight loads start as soon as
- * the experts are chosen; otherwise it is the two calls.  flags as for
- * moe_route (with MOE_F_INPUT_RMSNORM the experts see x_norm).
+ * moe_forward_w4a16 on the ids and weights it produced (topk_ids, topk_w,
+ * x_norm and out are all written; ids, weights and x_norm are those of
+ * moe_route bit for bit).  For one token (decode) the router, the top-k and
+ * the expert FFNs run as one launch whose routed weight loads start as soon
+ * as the experts are chosen; its output agrees with the two calls' within
+ * their rounding (the expert h is kept as scaled fp16 instead of a bf16
+ * pair).  Otherwise it is the two calls, unless MOE_F_ONE_LAUNCH asks for the
+ * one launch.  flags: MOE_F_INPUT_RMSNORM as for moe_route (the experts then
+ * see x_norm), MOE_F_ONE_LAUNCH.  Concurrent calls on one workspace race.
  * M = 0 is a no-op. */
 int moe_layer_w4a16(const moe_config* cfg /* host */, const float* router_w, const void* packed,
                     const uint16_t* x, int32_t M, uint32_t flags, uint16_t* x_norm,

@@ -1,7 +1,7 @@
 """GPU parity of moe_layer_w4a16, the whole layer in one call: the one-launch
-small-M path (router, top-k, shared and routed experts and the combine as
-workgroup roles of one grid) against the fp64 oracle, and against the
-separate moe_route + moe_forward_w4a16 calls bit for bit."""
+kernel (router, top-k, shared and routed experts and the output as workgroup
+roles of one grid; used for M = 1, and for larger M with MOE_F_ONE_LAUNCH)
+against the fp64 oracle, and its routing against moe_route bit for bit."""
 import dataclasses
 import sys
 
@@ -34,10 +34,12 @@ def ling():
     return DeviceLayer(synth.make_layer(synth.LING, 1), max_tokens=16)
 
 
-def _layer(dl, x_dev, flags=0, x_norm=None):
+def _layer(dl, x_dev, flags=None, x_norm=None):
     import torch
     from w4a16_grouped_quantized_amd import binding as B
     M = x_dev.shape[0]
+    if flags is None:  # the one-launch kernel at every M it supports
+        flags = B.MOE_F_ONE_LAUNCH
     ids = torch.full((M, dl.shape.top_k), -7, dtype=torch.int32, device="cuda")
     w = torch.full((M, dl.shape.top_k), -1.0, dtype=torch.float32, device="cuda")
     out = torch.empty((M, dl.shape.hidden), dtype=torch.bfloat16, device="cuda")
@@ -82,15 +84,22 @@ def test_layer_after_larger_calls(ling, oracle_mod):
 
 
 @pytest.mark.parametrize("M", [1, 3, 8])
-def test_layer_equals_route_then_forward(ling, M):
+def test_layer_equals_route_then_forward(ling, oracle_mod, M):
+    """The routing inside the launch is moe_route's bit for bit; both
+    outputs (one launch, and the separate calls) meet the oracle."""
     import torch
-    x_dev = to_dev_bf16(synth.make_tokens(synth.LING, 600 + M, M))
+    x = synth.make_tokens(synth.LING, 600 + M, M)
+    x_dev = to_dev_bf16(x)
     ids, w, out = _layer(ling, x_dev)
     r_ids, r_w = ling.route(x_dev)
     r_out = ling.forward(x_dev, r_ids, r_w)
     torch.cuda.synchronize()
+    assert ling.device_error() == 0
     assert torch.equal(ids, r_ids) and torch.equal(w, r_w)
-    assert torch.equal(out.view(torch.int16), r_out.view(torch.int16))
+    ref, bad = oracle_mod.forward(synth.LING, ling.layer, x, ids.cpu().numpy(), w.cpu().numpy().astype(np.float64))
+    assert bad == 0
+    check_out(from_dev_bf16(out), ref, f"one launch M={M}")
+    check_out(from_dev_bf16(r_out), ref, f"route + forward M={M}")
 
 
 def test_stages_match_oracle(ling, oracle_mod):
@@ -132,15 +141,14 @@ def test_layer_rmsnorm(ling, oracle_mod, M):
     y = synth.bf16_bits(np.random.default_rng(40 + M).standard_normal((M, shape.hidden)) * 7.0)
     y_dev = to_dev_bf16(y)
     xn = torch.empty_like(y_dev)
-    ids, w, out = _layer(ling, y_dev, flags=B.MOE_F_INPUT_RMSNORM, x_norm=xn)
+    ids, w, out = _layer(ling, y_dev, flags=B.MOE_F_INPUT_RMSNORM | B.MOE_F_ONE_LAUNCH, x_norm=xn)
     xn2 = torch.empty_like(y_dev)
     r_ids, r_w = ling.route(y_dev, flags=B.MOE_F_INPUT_RMSNORM, x_norm=xn2)
-    r_out = ling.forward(xn2, r_ids, r_w)
     torch.cuda.synchronize()
-    assert ling.device_error() == 0, f"device error word {ling.device_error()}"
+    err = ling.device_error()
+    assert err == 0, f"device error word {err}"
     assert torch.equal(xn.view(torch.int16), xn2.view(torch.int16))
     assert torch.equal(ids, r_ids) and torch.equal(w, r_w)
-    assert torch.equal(out.view(torch.int16), r_out.view(torch.int16))
     xin = from_dev_bf16(xn)
     ref_norm = oracle_mod.rmsnorm(y, 1e-6)
     assert np.abs(xin.astype(np.int32) - ref_norm.astype(np.int32)).max() <= 1

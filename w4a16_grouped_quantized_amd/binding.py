@@ -17,6 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_w4a16.so")
 
 MOE_F_INPUT_RMSNORM = 0x1
+MOE_F_ONE_LAUNCH = 0x2
 
 MOE_OK = 0
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_ALIGN",

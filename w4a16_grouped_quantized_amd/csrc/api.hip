@@ -179,9 +179,6 @@ int moe_forward_w4a16(const moe_config* cfg, const void* packed, const uint16_t*
   const uint8_t* pk = static_cast<const uint8_t*>(packed);
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (layer_supported(s, M))
-    return launched(launch_layer(s, pk, P, nullptr, x, M, false, false, kRmsEps, nullptr,
-                                 const_cast<int32_t*>(topk_ids), const_cast<float*>(topk_w), out, w8, L, st));
   rc = launched(launch_gate_up(s, pk, P, x, M, topk_ids, w8, L, st));
   if (rc != MOE_OK) return rc;
   return launched(launch_down(s, pk, P, M, topk_ids, topk_w, out, w8, L, st));
@@ -193,14 +190,15 @@ int moe_layer_w4a16(const moe_config* cfg, const float* router_w, const void* pa
   Shape s;
   int rc = check_cfg(cfg, &s);
   if (rc != MOE_OK) return rc;
-  if (M < 0 || (flags & ~MOE_F_INPUT_RMSNORM)) return MOE_ERR_SHAPE;
+  if (M < 0 || (flags & ~(MOE_F_INPUT_RMSNORM | MOE_F_ONE_LAUNCH))) return MOE_ERR_SHAPE;
   if (M == 0) return MOE_OK;
   const bool rms = (flags & MOE_F_INPUT_RMSNORM) != 0;
+  const bool one = M == 1 || (flags & MOE_F_ONE_LAUNCH) != 0;
   if (!router_w || !packed || !x || !topk_ids || !topk_w || !out || !ws || (rms && !x_norm)) return MOE_ERR_NULL;
   if (!aligned16(router_w) || !aligned16(packed) || !aligned16(x) || !aligned16(out) || !aligned16(ws) ||
       !aligned4(topk_ids) || !aligned4(topk_w) || (rms && !aligned16(x_norm)))
     return MOE_ERR_ALIGN;
-  if (layer_supported(s, M) && route_supported(s)) {
+  if (one && layer_supported(s, M) && route_supported(s)) {
     WsLayout L;
     rc = check_experts(cfg, &s, packed, x, M, topk_ids, topk_w, out, ws, ws_bytes, true, true, &L);
     if (rc != MOE_OK) return rc;
@@ -208,7 +206,7 @@ int moe_layer_w4a16(const moe_config* cfg, const float* router_w, const void* pa
     return launched(launch_layer(s, static_cast<const uint8_t*>(packed), P, router_w, x, M, true, rms, kRmsEps, x_norm,
                                  topk_ids, topk_w, out, static_cast<uint8_t*>(ws), L, static_cast<hipStream_t>(stream)));
   }
-  rc = moe_route(cfg, router_w, x, M, flags, x_norm, topk_ids, topk_w, ws, ws_bytes, stream);
+  rc = moe_route(cfg, router_w, x, M, flags & MOE_F_INPUT_RMSNORM, x_norm, topk_ids, topk_w, ws, ws_bytes, stream);
   if (rc != MOE_OK) return rc;
   return moe_forward_w4a16(cfg, packed, rms ? x_norm : x, M, topk_ids, topk_w, out, ws, ws_bytes, stream);
 }
@@ -264,7 +262,7 @@ const char* moe_build_info(void) {
          "route=wave-per-row-fp32+lastwg-topk|mfma-bf16x3(M>=33) "
          "gate_up=int4-dot2bf16-sgpr-act(GW20P4|GW2P2)+shared-bf16(KS-split,lastwg) "
          "down=int4-dot2bf16(GW6P2|GW1P1)+lastwg-combine "
-         "layer(M*k<=64)=one-launch(router, shared, routed gate_up, down+combine; tagged hand-offs) "
+         "layer(M=1, or M*k<=64 on request)=one-launch(router, shared, routed gate_up, down+combine; tagged hand-offs) "
          "prefill(M*k>=513)=grouped-mfma-f16-exact-int4(96-row items,xcd-aware)+shared-mfma-bf16 "
          "permute=multi-wg-stable-counting-sort "
          "max_experts=512 max_decode_slots=4096";
