@@ -200,6 +200,7 @@ def main():
     log(f"{steps} steps in {ms:.2f} ms (wall {wall * 1e3:.2f} ms): {ms_per_step * 1e3:.2f} us/step, "
         f"{gbs:.0f} GB/s, unique experts/step {uniq:.2f}")
 
+    one_launch = False
     if prefill:
         # route (router GEMM + top-k) and forward (permutation, grouped GEMMs,
         # combine) timed separately, eager, HIP events on the launch stream
@@ -234,8 +235,8 @@ def main():
         # that call alone over the same rotation of layer copies, replayed
         # between HIP events on the launch stream; duration per launch =
         # elapsed / n.  route = moe_route (k_route), forward = moe_forward_w4a16
-        # on the routed ids (k_layer without routing at this size), and the
-        # two stage kernels of the separate-call API.
+        # on the routed ids (k_gate_up then k_down), and those two kernels
+        # alone.
         stage_names = ("route", "forward", "gate_up", "down")
 
         def stage_graph(stage, n):
@@ -278,7 +279,8 @@ def main():
             " ".join(f"{nm} {v:.2f}" for nm, v in zip(stage_names, st)))
         stage = {nm: round(float(v), 3) for nm, v in zip(stage_names, st)}
         n_uniq = uniq if args.workload != "stack" else 8
-        if args.path == "layer":
+        one_launch = args.path == "layer" and M == 1
+        if one_launch:
             # the dominant kernel is the only one: k_layer, one launch per
             # layer; its duration per launch is the timed region / launches
             launches = n_layers if args.workload == "stack" else 1
@@ -286,10 +288,12 @@ def main():
             bytes_launch = bytes_per_step / launches
             kernel = "k_layer (one launch per layer: router, top-k, shared and routed experts, output)"
         else:
-            # separate calls: the dominant kernel is moe_forward_w4a16's k_layer
-            us_launch = float(st[1])
-            bytes_launch = step_bytes(int(round(n_uniq)), M) - ROUTER_BYTES
-            kernel = "k_layer without routing (moe_forward_w4a16: shared and routed experts, output)"
+            # separate kernels (k_route, k_gate_up, k_down); the dominant one
+            # is k_gate_up: the gate_up weights of the step's distinct experts
+            # and of the shared expert, and the step's token rows
+            us_launch = float(st[2])
+            bytes_launch = n_uniq * EXPERT_GU_BYTES + SHARED_GU_BYTES + M * 2560 * 2
+            kernel = "k_gate_up (routed INT4 gate_up + SiLU of the step's distinct experts, shared gate_up)"
         achieved = bytes_launch / (us_launch * 1e-6) / 1e9
         roof = {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
@@ -306,7 +310,7 @@ def main():
         log(f"calibration copy: {args.calib_copy_mib} MiB x 2")
 
     if roof.get("traffic") is None:
-        roof["traffic"] = measured_traffic(WORKLOAD_NAMES[args.workload]) if args.path == "layer" or prefill else None
+        roof["traffic"] = measured_traffic(WORKLOAD_NAMES[args.workload]) if one_launch or prefill else None
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -9,8 +9,8 @@ import numpy as np
 import pytest
 
 from w4a16_grouped_quantized_amd import synth
-from parity import (DeviceLayer, bf16_f64, check_ids, check_out, from_dev_bf16, run_and_check,
-                    to_dev_bf16)
+from parity import (DeviceLayer, bf16_f64, bf16_half_ulp, check_ids, check_out, from_dev_bf16,
+                    run_and_check, to_dev_bf16)
 
 pytestmark = pytest.mark.gpu
 
@@ -332,3 +332,87 @@ def test_ling_many_tokens_caller_ids(ling_big, oracle_mod):
     ref, bad = oracle_mod.forward(shape, ling_big.layer, x, ids_bad, w.astype(np.float64))
     assert bad == 2
     check_out(from_dev_bf16(out), ref, "many tokens, invalid ids contribute zero")
+
+
+# ------------------------------------------------------------------ one-hot tokens
+
+def _onehot_tokens(shape, positions):
+    x = np.zeros((len(positions), shape.hidden), np.uint16)
+    for t, k in enumerate(positions):
+        x[t, k] = 0x3F80  # bf16 1.0
+    return x
+
+
+def _check_tight(out_bits, ref, tol, what):
+    """|gpu - oracle| - half a bf16 ulp <= tol * rms: with a one-hot token every
+    gate and up row of an expert sums exactly one dequantised weight, so a
+    wrong nibble, nibble order, scale or row lands as an O(1) error."""
+    got = bf16_f64(out_bits)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    excess = float(np.max(np.abs(got - ref) - bf16_half_ulp(ref)))
+    assert excess <= tol * rms, f"{what}: excess {excess / rms:.3e} * rms > {tol}"
+    _say(f"{what}: max(|err| - half bf16 ulp)/rms = {excess / rms:.3e} (bound {tol})")
+
+
+# inputs at both nibble positions of a byte, at group and tile edges, first and last
+ONEHOT_POS = [0, 1, 7, 8, 31, 32, 33, 255, 1279, 1280, 2527, 2559]
+
+
+def test_onehot_tokens_every_path(ling_big, oracle_mod):
+    """One-hot tokens through each kernel path with caller ids, against the
+    oracle at bounds derived from each path's own rounding: the decode and
+    verify kernels keep h to about 16 bits (a bf16 hi + lo pair) and sum in
+    fp32 (bound 1e-4 * rms); the grouped-GEMM path rounds h to fp16, 2^-12
+    relative per element (bound 4e-3 * rms)."""
+    import torch
+    shape = synth.LING
+    xs = _onehot_tokens(shape, ONEHOT_POS)
+    n = len(ONEHOT_POS)
+    rng = np.random.default_rng(77)
+    # decode (M = 1) and a verify-sized call (M = n): separate kernels
+    ids = np.stack([rng.choice(shape.n_experts, shape.top_k, replace=False) for _ in range(n)]).astype(np.int32)
+    w = rng.random((n, shape.top_k)).astype(np.float32)
+    ref, bad = oracle_mod.forward(shape, ling_big.layer, xs, ids, w.astype(np.float64))
+    assert bad == 0
+    for t in (0, 1, n - 1):
+        out = ling_big.forward(to_dev_bf16(xs[t:t + 1]), torch.from_numpy(ids[t:t + 1]).cuda(),
+                               torch.from_numpy(w[t:t + 1]).cuda())
+        torch.cuda.synchronize()
+        _check_tight(from_dev_bf16(out), ref[t:t + 1], 1e-4, f"one-hot decode, input {ONEHOT_POS[t]}")
+    out = ling_big.forward(to_dev_bf16(xs), torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda())
+    torch.cuda.synchronize()
+    _check_tight(from_dev_bf16(out), ref, 1e-4, f"one-hot verify-sized call, M={n}")
+    # grouped GEMMs: the same tokens repeated to M = 8n (M k >= 513), new ids per row
+    reps = 8
+    xb = np.tile(xs, (reps, 1))
+    idb = np.stack([rng.choice(shape.n_experts, shape.top_k, replace=False) for _ in range(n * reps)]).astype(np.int32)
+    wb = rng.random((n * reps, shape.top_k)).astype(np.float32)
+    refb, bad = oracle_mod.forward(shape, ling_big.layer, xb, idb, wb.astype(np.float64))
+    assert bad == 0
+    out = ling_big.forward(to_dev_bf16(xb), torch.from_numpy(idb).cuda(), torch.from_numpy(wb).cuda())
+    torch.cuda.synchronize()
+    assert ling_big.device_error() == 0
+    _check_tight(from_dev_bf16(out), refb, 4e-3, f"one-hot grouped GEMMs, M={n * reps}")
+
+
+def test_onehot_token_one_launch_layer(ling_big, oracle_mod):
+    """The one-launch layer (routing inside) on one-hot tokens: ids checked as
+    in every parity test, the output at the fp16-h bound (4e-3 * rms)."""
+    import torch
+    from w4a16_grouped_quantized_amd import binding as B
+    shape = synth.LING
+    for k in (0, 33, 2559):
+        x = _onehot_tokens(shape, [k])
+        ids = torch.empty((1, shape.top_k), dtype=torch.int32, device="cuda")
+        w = torch.empty((1, shape.top_k), dtype=torch.float32, device="cuda")
+        out = torch.empty((1, shape.hidden), dtype=torch.bfloat16, device="cuda")
+        B.layer(ling_big.cfg, ling_big.dev.router_w, ling_big.dev.packed, to_dev_bf16(x), ids, w, out,
+                ling_big.ws.buf)
+        torch.cuda.synchronize()
+        assert ling_big.device_error() == 0
+        ids_g, w_g = ids.cpu().numpy(), w.cpu().numpy()
+        ids_o, _, gap, logits_o = oracle_mod.route(shape, ling_big.layer.router_w, x)
+        w_ref = check_ids(shape, ids_g, w_g, ids_o, gap, logits_o)
+        ref, bad = oracle_mod.forward(shape, ling_big.layer, x, ids_g, w_ref)
+        assert bad == 0
+        _check_tight(from_dev_bf16(out), ref, 4e-3, f"one-hot one-launch layer, input {k}")

@@ -147,7 +147,8 @@ struct PfLayout : WsHeader {
   size_t perm, inv;                 // int32 [S]: pair at each sorted position, sorted position of each pair
   size_t ghist;                     // int32 [perm_groups(S)][E]
   size_t tile_e, tile_j, ntile;     // int32 [items], [items], [1]: work items (expert, row block)
-  size_t xh, rexp;                  // fp16 [M][H] scaled rows of x, int32 [M] their exponents
+  size_t xh, rexp;                  // fp16 [M][H] scaled rows of x; int32 [M][2]: the exponent r of each
+                                    // row's scaling and the exponent bound tx of its squared L2 norm
   size_t hbuf;                      // fp16 [S][I] scaled h per sorted position
   size_t hsh;                       // bf16 [2][M][I] shared-expert h as (hi, lo) planes
   size_t y, ysh;                    // fp16 [S][H] per sorted position (scaled), fp32 [M][H]
@@ -173,7 +174,7 @@ inline PfLayout pf_layout(int H, int E, int k, int I, int has_shared, int M) {
   w.tile_j = take((size_t)w.items * 4);
   w.ntile = take(4);
   w.xh = take((size_t)M * H * 2);
-  w.rexp = take((size_t)M * 4);
+  w.rexp = take((size_t)M * 8);
   w.hbuf = take(S * I * 2);
   w.hsh = take(has_shared ? (size_t)2 * M * I * 2 : 0);
   w.y = take(S * H * 2);
@@ -284,6 +285,12 @@ __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
   return v;
 }
 

@@ -22,7 +22,7 @@
 // non-negative values, used by the many-token kernels to scale fp16 operands
 // by powers of two):
 //   [0] max |scale| of gate_up, [1] max |scale| of down,
-//   [2] max over r < I of ||gate row r||_1 * ||up row r||_1 (dequantised),
+//   [2] max over r < I of ||gate row r||_2 * ||up row r||_2 (dequantised),
 //   [3] max over the down rows of ||down row||_1 (dequantised).
 #pragma once
 #include <stddef.h>

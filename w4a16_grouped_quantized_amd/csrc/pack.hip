@@ -77,7 +77,7 @@ __device__ __forceinline__ void max_bits(uint32_t* p, float v) {
 }
 
 // One wavefront per gate row r (and its up row I + r) of one expert: the
-// dequantised L1 norms of both rows (lane l takes groups l, l + 64, ...),
+// dequantised L2 norms of both rows (lane l takes groups l, l + 64, ...),
 // their product into word 2, and the largest |scale| into word 0.
 __global__ __launch_bounds__(256) void k_pack_meta_gu(const uint8_t* __restrict__ q, const uint16_t* __restrict__ sc,
                                                       uint32_t* __restrict__ meta, int H, int I) {
@@ -93,17 +93,20 @@ __global__ __launch_bounds__(256) void k_pack_meta_gu(const uint8_t* __restrict_
     for (int g = lane; g < GK; g += kWave) {
       const uint4 w = *reinterpret_cast<const uint4*>(q + row * (H / 2) + (size_t)g * 16);
       const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
-      int sum = 0;
+      int sum = 0;  // sum of q^2 over the group (exact)
 #pragma unroll
       for (int d = 0; d < 4; ++d)
 #pragma unroll
-        for (int n = 0; n < 8; ++n) sum += abs((int)((wd[d] >> (4 * n)) & 0xFu) - 8);
+        for (int n = 0; n < 8; ++n) {
+          const int qv = (int)((wd[d] >> (4 * n)) & 0xFu) - 8;
+          sum += qv * qv;
+        }
       const float s = fabsf(bf16_to_f32(sc[row * GK + g]));
-      norm[half] += s * (float)sum;
+      norm[half] += s * s * (float)sum;
       smax = fmaxf(smax, s);
     }
   }
-  const float prod = wave_sum(norm[0]) * wave_sum(norm[1]);
+  const float prod = sqrtf(wave_sum(norm[0])) * sqrtf(wave_sum(norm[1]));
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) smax = fmaxf(smax, __shfl_xor(smax, off, 64));
   if (lane == 0) {

@@ -26,10 +26,14 @@
 // fused result is exact in fp16's 11, and 2^p (per expert, from the largest
 // |scale|) keeps |q s'| <= 2^15.  The products of fp16 operands are exact in
 // the fp32 accumulators; the powers of two are taken out in the epilogues.
-// Bound on h: |g|, |u| <= max|x_t| * ||row||_1 and |silu(g)| <= |g|, so
-// |h| <= 2^(2 r_t + 30) * N_e with N_e = max_r ||gate_r||_1 ||up_r||_1
-// (computed when the weights are packed); sigma = 2 r_t + 16 + (exponent of
-// N_e) + 1 puts |h| 2^-sigma below 2^13, and h keeps fp16's 11 bits.
+// Bound on h: |g| <= ||x_t||_2 ||gate_r||_2 and |u| <= ||x_t||_2 ||up_r||_2
+// (Cauchy-Schwarz) and |silu(g)| <= |g|, so |h| <= ||x_t||_2^2 L_e with
+// L_e = max_r ||gate_r||_2 ||up_r||_2 (computed when the weights are packed).
+// With ||x_t||_2^2 < 2^tx_t and L_e < 2^le_e, sigma = tx_t + le_e - 13 puts
+// |h| 2^-sigma below 2^13; h keeps fp16's 11 significant bits wherever
+// |h| 2^-sigma >= 2^-14.
+// The L2 bound sits within a factor of about sqrt(K) of typical values for
+// dense and for one-hot rows alike (an L1 bound with max |x| would not).
 #include <type_traits>
 
 #include "launch.hpp"
@@ -47,6 +51,10 @@ __device__ __forceinline__ int exp_above(float v) {
   return ex == 0 ? -126 : ex - 126;
 }
 
+// e with v < 2^e for a non-negative v computed by fp32 sums of at most a few
+// thousand exact terms: the factor 1 + 2^-10 covers their rounding.
+__device__ __forceinline__ int exp_bound(float v) { return exp_above(v * 1.0009765625f); }
+
 // C[m][n] of a 32x32 MFMA block lives in lane n + 32*((m/4)%2), slot (m%4) + 4*(m/8).
 __device__ __forceinline__ int c_row(int lane, int slot) { return 8 * (slot >> 2) + 4 * (lane >> 5) + (slot & 3); }
 
@@ -60,25 +68,30 @@ __device__ __forceinline__ int k8_pos(int i) { return 2 * (i & 3) + (i >> 2); }
 
 __global__ __launch_bounds__(kBlock) void k_pf_xprep(const uint16_t* __restrict__ x, int H,
                                                      _Float16* __restrict__ xh, int32_t* __restrict__ rexp) {
-  __shared__ float red[kWavesPerBlock];
+  __shared__ float red[2][kWavesPerBlock];
   const int t = blockIdx.x, tid = threadIdx.x;
   const uint4* row = reinterpret_cast<const uint4*>(x + (size_t)t * H);
   const int nch = H / 8;
-  float m = 0.f;
+  float m = 0.f, ss = 0.f;
   for (int c = tid; c < nch; c += kBlock) {
     const uint4 v = row[c];
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      m = fmaxf(m, fabsf(bf16_to_f32(w[d] & 0xFFFFu)));
-      m = fmaxf(m, fabsf(bf16_to_f32(w[d] >> 16)));
+      const float lo = bf16_to_f32(w[d] & 0xFFFFu), hi = bf16_to_f32(w[d] >> 16);
+      m = fmaxf(m, fmaxf(fabsf(lo), fabsf(hi)));
+      ss = fmaf(lo, lo, fmaf(hi, hi, ss));
     }
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  if ((tid & 63) == 0) red[tid >> 6] = m;
+  m = wave_max(m);
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = m;
+    red[1][tid >> 6] = ss;
+  }
   __syncthreads();
-  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  m = fmaxf(fmaxf(red[0][0], red[0][1]), fmaxf(red[0][2], red[0][3]));
+  ss = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
   const int r = exp_above(m) - 15;  // max |x| * 2^-r < 2^15
   for (int c = tid; c < nch; c += kBlock) {
     const uint4 v = row[c];
@@ -94,7 +107,10 @@ __global__ __launch_bounds__(kBlock) void k_pf_xprep(const uint16_t* __restrict_
     for (int j = 0; j < 8; ++j) o[j] = (_Float16)f[(j >> 1) + 4 * (j & 1)];
     *reinterpret_cast<f16x8_t*>(xh + (size_t)t * H + 8 * c) = o;
   }
-  if (tid == 0) rexp[t] = r;
+  if (tid == 0) {
+    rexp[2 * t] = r;
+    rexp[2 * t + 1] = exp_bound(ss);  // ||x_t||_2^2 < 2^tx
+  }
 }
 
 // ------------------------------------------------------------------ grouped GEMMs
@@ -119,7 +135,7 @@ struct GgArgs {
   const int32_t* __restrict__ ntile;
   // activations
   const _Float16* __restrict__ xh;    // [M][H] scaled x, K order of k8_pos
-  const int32_t* __restrict__ rexp;   // [M]
+  const int32_t* __restrict__ rexp;   // [M][2]: r (x scaling) and tx (bound of ||x||^2) per token
   const _Float16* __restrict__ hbuf;  // [S][I] scaled h per sorted position, K order of k8_pos
   const uint16_t* __restrict__ x;     // [M][H] bf16
   const uint16_t* __restrict__ hsh;   // [2][M][I] bf16 (hi, lo)
@@ -427,11 +443,11 @@ __device__ __forceinline__ void gg_item(const GgArgs& a, int b, uint16_t (*sA)[k
     if (it.base >= a.M) return;
     it.nrow = min(C::ROWS, a.M - it.base);
   }
-  int ne = 0;
+  int le = 0;
   if constexpr (C::ROUTED) {
     const uint32_t* mt = a.meta + (size_t)it.e * kMetaWords;
     it.p = min(12 - exp_above(__uint_as_float(mt[a.meta_word])), 126);
-    ne = exp_above(__uint_as_float(mt[2])) + 1;
+    le = exp_bound(__uint_as_float(mt[2]));
     it.ey = 1 - it.p - exp_above(__uint_as_float(mt[3]));
   }
   // ---- row tables: A source row and the exponents of each row
@@ -439,14 +455,13 @@ __device__ __forceinline__ void gg_item(const GgArgs& a, int b, uint16_t (*sA)[k
     const int rr = tid < it.nrow ? tid : 0;  // padding rows repeat row 0; their results are dropped
     if constexpr (KIND == GG_RGU) {
       const int tok = a.perm[it.base + rr] / a.k;
-      const int r = a.rexp[tok];
       sSrc[tid] = tok;
-      sExp[tid] = r;
-      sSig[tid] = 2 * r + 16 + ne;
+      sExp[tid] = a.rexp[2 * tok];
+      sSig[tid] = a.rexp[2 * tok + 1] + le - 13;
     } else if constexpr (KIND == GG_RDN) {
       const int tok = a.perm[it.base + rr] / a.k;
       sSrc[tid] = it.base + rr;
-      sExp[tid] = 2 * a.rexp[tok] + 16 + ne;
+      sExp[tid] = a.rexp[2 * tok + 1] + le - 13;
     } else {
       sSrc[tid] = it.base + rr;
     }
@@ -766,7 +781,7 @@ struct CombineArgs {
   const float* __restrict__ topk_w;
   const int32_t* __restrict__ inv;     // sorted position of each pair
   const _Float16* __restrict__ y;      // [S][H] per sorted position, scaled (see GgArgs::y)
-  const int32_t* __restrict__ rexp;    // [M] row exponents of x
+  const int32_t* __restrict__ rexp;    // [M][2] per token: r, tx (the h exponent sigma = tx + le - 13)
   const uint32_t* __restrict__ meta;   // per-expert range data
   const float* __restrict__ ysh;    // [M][H]
   uint16_t* __restrict__ out;
@@ -789,7 +804,7 @@ __global__ __launch_bounds__(kBlock) void k_pf_combine(const CombineArgs a) {
     const int e = a.ids[p];
     if (e < 0 || e >= a.E) { bad = true; continue; }
     const uint32_t* mt = a.meta + (size_t)e * kMetaWords;
-    const int sigma = 2 * a.rexp[t] + 16 + exp_above(__uint_as_float(mt[2])) + 1;
+    const int sigma = a.rexp[2 * t + 1] + exp_bound(__uint_as_float(mt[2])) - 13;
     const float wv = ldexpf(a.topk_w[p], sigma + exp_above(__uint_as_float(mt[3])) - 1);
     const uint2 raw = *reinterpret_cast<const uint2*>(a.y + (size_t)a.inv[p] * a.H + n0);
     const f16x2_t v01 = __builtin_bit_cast(f16x2_t, raw.x), v23 = __builtin_bit_cast(f16x2_t, raw.y);
@@ -811,8 +826,9 @@ __global__ __launch_bounds__(kBlock) void k_pf_combine(const CombineArgs a) {
 
 bool prefill_supported(const Shape& s) {
   // K of both GEMMs a whole number of 256-input blocks (four 64-K steps);
-  // weight tiles of 64 rows; router tiles of 64 experts
-  return s.H % 256 == 0 && s.I % 256 == 0 && s.E % 64 == 0;
+  // weight tiles of 64 rows; router tiles of 64 experts; at most 8192 terms
+  // in the fp32 norm sums that the h exponent bounds (exp_bound's slack)
+  return s.H % 256 == 0 && s.I % 256 == 0 && s.E % 64 == 0 && s.H <= 8192 && s.I <= 8192;
 }
 
 static int ceil_div(int a, int b) { return (a + b - 1) / b; }
