@@ -788,38 +788,70 @@ struct CombineArgs {
   int32_t* __restrict__ err;
 };
 
-// One thread per 4 outputs of one token: the y rows of the token's k slots,
-// each back at its true scale 2^(sigma + e2 - 1) and weighted, are summed in
-// slot order, then the shared expert's row.
+// One workgroup per token: the first k threads look up each slot's sorted
+// row and the factor that takes its y back to the true scale 2^(sigma + e2 -
+// 1) and weights it; then each thread sums 8 outputs over the slots in slot
+// order (16-byte loads of every slot's row issued together), adds the shared
+// expert's row and rounds to bf16.
 __global__ __launch_bounds__(kBlock) void k_pf_combine(const CombineArgs a) {
-  const size_t q = (size_t)blockIdx.x * kBlock + threadIdx.x;  // quad index
-  const size_t per_tok = a.H / 4;
-  if (q >= (size_t)a.M * per_tok) return;
-  const int t = (int)(q / per_tok);
-  const int n0 = (int)(q % per_tok) * 4;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  bool bad = false;
-  for (int jj = 0; jj < a.k; ++jj) {
-    const int p = t * a.k + jj;
+  __shared__ int srow[kMaxTopK];
+  __shared__ float swv[kMaxTopK];
+  __shared__ int sbad;
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (tid == 0) sbad = 0;
+  __syncthreads();
+  if (tid < a.k) {
+    const int p = t * a.k + tid;
     const int e = a.ids[p];
-    if (e < 0 || e >= a.E) { bad = true; continue; }
-    const uint32_t* mt = a.meta + (size_t)e * kMetaWords;
-    const int sigma = a.rexp[2 * t + 1] + exp_bound(__uint_as_float(mt[2])) - 13;
-    const float wv = ldexpf(a.topk_w[p], sigma + exp_above(__uint_as_float(mt[3])) - 1);
-    const uint2 raw = *reinterpret_cast<const uint2*>(a.y + (size_t)a.inv[p] * a.H + n0);
-    const f16x2_t v01 = __builtin_bit_cast(f16x2_t, raw.x), v23 = __builtin_bit_cast(f16x2_t, raw.y);
-    acc.x = fmaf(wv, (float)v01[0], acc.x); acc.y = fmaf(wv, (float)v01[1], acc.y);
-    acc.z = fmaf(wv, (float)v23[0], acc.z); acc.w = fmaf(wv, (float)v23[1], acc.w);
+    if (e < 0 || e >= a.E) {
+      srow[tid] = -1;
+      swv[tid] = 0.f;
+      sbad = 1;
+    } else {
+      const uint32_t* mt = a.meta + (size_t)e * kMetaWords;
+      const int sigma = a.rexp[2 * t + 1] + exp_bound(__uint_as_float(mt[2])) - 13;
+      srow[tid] = a.inv[p];
+      swv[tid] = ldexpf(a.topk_w[p], sigma + exp_above(__uint_as_float(mt[3])) - 1);
+    }
   }
-  if (a.has_shared) {
-    const float4 v = *reinterpret_cast<const float4*>(a.ysh + (size_t)t * a.H + n0);
-    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  __syncthreads();
+  for (int c = tid; c < a.H / 8; c += kBlock) {
+    const int n0 = 8 * c;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < a.k; j0 += 8) {  // slots in batches of 8, loads first
+      uint4 raw[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = j0 + j < a.k ? srow[j0 + j] : -1;
+        raw[j] = r >= 0 ? *reinterpret_cast<const uint4*>(a.y + (size_t)r * a.H + n0) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (j0 + j >= a.k || srow[j0 + j] < 0) continue;
+        const float wv = swv[j0 + j];
+        const uint32_t d[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f16x2_t v = __builtin_bit_cast(f16x2_t, d[q]);
+          acc[2 * q] = fmaf(wv, (float)v[0], acc[2 * q]);
+          acc[2 * q + 1] = fmaf(wv, (float)v[1], acc[2 * q + 1]);
+        }
+      }
+    }
+    if (a.has_shared) {
+      const float4 v0 = *reinterpret_cast<const float4*>(a.ysh + (size_t)t * a.H + n0);
+      const float4 v1 = *reinterpret_cast<const float4*>(a.ysh + (size_t)t * a.H + n0 + 4);
+      acc[0] += v0.x; acc[1] += v0.y; acc[2] += v0.z; acc[3] += v0.w;
+      acc[4] += v1.x; acc[5] += v1.y; acc[6] += v1.z; acc[7] += v1.w;
+    }
+    uint4 o;
+    o.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
+    o.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+    o.z = (uint32_t)f32_to_bf16(acc[4]) | ((uint32_t)f32_to_bf16(acc[5]) << 16);
+    o.w = (uint32_t)f32_to_bf16(acc[6]) | ((uint32_t)f32_to_bf16(acc[7]) << 16);
+    *reinterpret_cast<uint4*>(a.out + (size_t)t * a.H + n0) = o;
   }
-  uint2 o;
-  o.x = (uint32_t)f32_to_bf16(acc.x) | ((uint32_t)f32_to_bf16(acc.y) << 16);
-  o.y = (uint32_t)f32_to_bf16(acc.z) | ((uint32_t)f32_to_bf16(acc.w) << 16);
-  *reinterpret_cast<uint2*>(a.out + (size_t)t * a.H + n0) = o;
-  if (bad) atomicOr(a.err, 1);
+  if (tid == 0 && sbad) atomicOr(a.err, 1);
 }
 
 // ------------------------------------------------------------------ host side
@@ -911,8 +943,7 @@ hipError_t launch_prefill_forward(const Shape& s, const uint8_t* packed, const P
   }
   if ((e = hipGetLastError()) != hipSuccess) return e;
   CombineArgs c{M, s.E, s.k, s.H, s.has_shared, ids, w, i32(P.inv), a.y, i32(P.rexp), a.meta, a.ysh, out, err};
-  const size_t quads = (size_t)M * (s.H / 4);
-  hipLaunchKernelGGL(k_pf_combine, dim3((unsigned)((quads + kBlock - 1) / kBlock)), dim3(kBlock), 0, st, c);
+  hipLaunchKernelGGL(k_pf_combine, dim3((unsigned)M), dim3(kBlock), 0, st, c);
   return hipGetLastError();
 }
 
