@@ -180,7 +180,7 @@ int moe_get_device_error(void* ws, void* stream, int32_t* code_host /* host */);
 
 const char* moe_status_string(int status);
 
-/* Static description of the build: target arch, kernel variants and the
+/* Static description of the compiled library: target arch, kernel variants and the
  * packed-layout tag, for logging next to every measurement. */
 const char* moe_build_info(void);
 
