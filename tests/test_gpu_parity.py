@@ -416,3 +416,48 @@ def test_onehot_token_one_launch_layer(ling_big, oracle_mod):
         ref, bad = oracle_mod.forward(shape, ling_big.layer, x, ids_g, w_ref)
         assert bad == 0
         _check_tight(from_dev_bf16(out), ref, 4e-3, f"one-hot one-launch layer, input {k}")
+
+
+def _outlier_tokens(shape, seed, M):
+    """N(0,1) tokens with a few channels 100-300 times larger, as in the
+    hidden states of trained transformers (a handful of massive channels)."""
+    x = synth.make_tokens(shape, seed, M)
+    rng = np.random.default_rng(seed)
+    xf = synth.bf16_bits_to_f32(x).astype(np.float32)
+    chans = rng.choice(shape.hidden, 4, replace=False)
+    xf[:, chans] = rng.choice([-1.0, 1.0], (M, 4)) * rng.uniform(100.0, 300.0, (M, 4))
+    return synth.bf16_bits(xf)
+
+
+@pytest.mark.parametrize("M", [1, 4, 80])
+def test_outlier_channel_tokens(ling_big, oracle_mod, M):
+    """Tokens with massive channels through routing and every expert path
+    (M = 1 and 4: small-M kernels; M = 80: router GEMM and grouped GEMMs),
+    at the parity bound."""
+    x = _outlier_tokens(synth.LING, 500 + M, M)
+    ratio = run_and_check(ling_big, oracle_mod, x, f"outlier channels M={M}")
+    _say(f"outlier channels M={M}: max|err|/rms = {ratio:.3e}")
+
+
+def test_outlier_channel_token_one_launch_layer(ling_big, oracle_mod):
+    """The one-launch layer (routing inside) on tokens with massive channels."""
+    import torch
+    from w4a16_grouped_quantized_amd import binding as B
+    shape = synth.LING
+    for seed in (601, 602, 603):
+        x = _outlier_tokens(shape, seed, 1)
+        ids = torch.empty((1, shape.top_k), dtype=torch.int32, device="cuda")
+        w = torch.empty((1, shape.top_k), dtype=torch.float32, device="cuda")
+        out = torch.empty((1, shape.hidden), dtype=torch.bfloat16, device="cuda")
+        B.layer(ling_big.cfg, ling_big.dev.router_w, ling_big.dev.packed, to_dev_bf16(x), ids, w, out,
+                ling_big.ws.buf)
+        torch.cuda.synchronize()
+        assert ling_big.device_error() == 0
+        ids_g, w_g = ids.cpu().numpy(), w.cpu().numpy()
+        ids_o, _, gap, logits_o = oracle_mod.route(shape, ling_big.layer.router_w, x)
+        w_ref = check_ids(shape, ids_g, w_g, ids_o, gap, logits_o)
+        ref, bad = oracle_mod.forward(shape, ling_big.layer, x, ids_g, w_ref)
+        assert bad == 0
+        ratio = check_out(from_dev_bf16(out), ref, f"outlier channels, one-launch layer, seed {seed}")
+        _say(f"outlier channels one-launch layer seed {seed}: max|err|/rms = {ratio:.3e}, "
+             f"beyond the bf16 store {check_out.last_excess:.3e}")
