@@ -177,18 +177,20 @@ __device__ __forceinline__ void topk_token(const RouteArgs& a, int t, int lane, 
 // The RMSNorm divisor of a token from its sum of squares (unit gain).
 __device__ __forceinline__ float rms_divisor(float ss, int H, float eps) { return sqrtf(ss / (float)H + eps); }
 
-// One wavefront's view of token t: lane l holds inputs 256*i + 4*l .. +3 as
-// float (raw, or RMS-normalised and rounded to bf16); `packed` receives the
-// same values as bf16 pairs.  The sum of squares runs in a fixed order
-// (i, then the 4 inputs, then the xor butterfly), so every wavefront that
-// calls this gets the same bits.
+// Lane l's inputs 256*i + 4*l .. +3 of a token row, as bf16 pairs.
 template <int NI>
-__device__ __forceinline__ void load_token(const uint16_t* __restrict__ xt, int H, int lane, bool rmsnorm, float eps,
-                                           float (&xv)[NI][4], uint2 (&packed)[NI]) {
+__device__ __forceinline__ void fetch_token(const uint16_t* __restrict__ xt, int lane, uint2 (&packed)[NI]) {
+#pragma unroll
+  for (int i = 0; i < NI; ++i) packed[i] = *reinterpret_cast<const uint2*>(xt + 256 * i + 4 * lane);
+}
+
+// The second half of load_token: `packed` (as fetched) to floats, normalised
+// when asked (then `packed` is rewritten with the normalised bf16 values).
+template <int NI>
+__device__ __forceinline__ void decode_token(int H, bool rmsnorm, float eps, float (&xv)[NI][4], uint2 (&packed)[NI]) {
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const uint2 v = *reinterpret_cast<const uint2*>(xt + 256 * i + 4 * lane);
-    packed[i] = v;
+    const uint2 v = packed[i];
     xv[i][0] = __uint_as_float(v.x << 16);
     xv[i][1] = __uint_as_float(v.x & 0xFFFF0000u);
     xv[i][2] = __uint_as_float(v.y << 16);
@@ -215,9 +217,23 @@ __device__ __forceinline__ void load_token(const uint16_t* __restrict__ xt, int 
   }
 }
 
+// One wavefront's view of token t: lane l holds inputs 256*i + 4*l .. +3 as
+// float (raw, or RMS-normalised and rounded to bf16); `packed` receives the
+// same values as bf16 pairs.  The sum of squares runs in a fixed order
+// (i, then the 4 inputs, then the xor butterfly), so every wavefront that
+// calls this gets the same bits.
+template <int NI>
+__device__ __forceinline__ void load_token(const uint16_t* __restrict__ xt, int H, int lane, bool rmsnorm, float eps,
+                                           float (&xv)[NI][4], uint2 (&packed)[NI]) {
+  fetch_token<NI>(xt, lane, packed);
+  decode_token<NI>(H, rmsnorm, eps, xv, packed);
+}
+
 // Logits of router row e for every token (one wavefront, rows past E load
 // row E-1 and store nothing).  The row stays in registers while the
-// wavefront walks the tokens; `writer` also stores the normalised tokens.
+// wavefront walks the tokens, whose inputs are fetched kRouteBatch at a time
+// (one memory round trip per batch); `writer` also stores the normalised
+// tokens.
 // With keys, each logit is stored as its order-preserving key (never 0)
 // instead of into a.logits.
 template <int NI>
@@ -227,30 +243,40 @@ __device__ __forceinline__ void router_row(const RouteArgs& a, int e, int lane, 
   float4 wr[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) wr[i] = *reinterpret_cast<const float4*>(a.wr + (size_t)er * a.H + 256 * i + 4 * lane);
-  for (int t = 0; t < a.M; ++t) {
-    float xv[NI][4];
-    uint2 packed[NI];
-    load_token<NI>(a.x + (size_t)t * a.H, a.H, lane, a.rmsnorm != 0, a.eps, xv, packed);
-    if (a.rmsnorm && writer) {
+  constexpr int kRouteBatch = 4;
+  for (int t0 = 0; t0 < a.M; t0 += kRouteBatch) {
+    uint2 batch[kRouteBatch][NI];
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
-        *reinterpret_cast<uint2*>(a.x_norm + (size_t)t * a.H + 256 * i + 4 * lane) = packed[i];
-    }
-    float acc = 0.f;
+    for (int b = 0; b < kRouteBatch; ++b)
+      if (t0 + b < a.M) fetch_token<NI>(a.x + (size_t)(t0 + b) * a.H, lane, batch[b]);
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      acc = fmaf(wr[i].x, xv[i][0], acc);
-      acc = fmaf(wr[i].y, xv[i][1], acc);
-      acc = fmaf(wr[i].z, xv[i][2], acc);
-      acc = fmaf(wr[i].w, xv[i][3], acc);
-    }
-    acc = wave_sum(acc);
-    if (has_row && lane == 0) {
-      if (keys) {
-        const uint32_t key = sort_key(acc);  // 0 only for one NaN pattern: stored as the lowest key instead
-        st_coherent(reinterpret_cast<int32_t*>(&keys[(size_t)t * a.E + e]), (int32_t)(key ? key : 1u));
+    for (int b = 0; b < kRouteBatch; ++b) {
+      const int t = t0 + b;
+      if (t >= a.M) break;
+      float xv[NI][4];
+      uint2 (&packed)[NI] = batch[b];
+      decode_token<NI>(a.H, a.rmsnorm != 0, a.eps, xv, packed);
+      if (a.rmsnorm && writer) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+          *reinterpret_cast<uint2*>(a.x_norm + (size_t)t * a.H + 256 * i + 4 * lane) = packed[i];
       }
-      else st_coherent(&a.logits[(size_t)t * a.E + e], acc);
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        acc = fmaf(wr[i].x, xv[i][0], acc);
+        acc = fmaf(wr[i].y, xv[i][1], acc);
+        acc = fmaf(wr[i].z, xv[i][2], acc);
+        acc = fmaf(wr[i].w, xv[i][3], acc);
+      }
+      acc = wave_sum(acc);
+      if (has_row && lane == 0) {
+        if (keys) {
+          const uint32_t key = sort_key(acc);  // 0 only for one NaN pattern: stored as the lowest key instead
+          st_coherent(reinterpret_cast<int32_t*>(&keys[(size_t)t * a.E + e]), (int32_t)(key ? key : 1u));
+        }
+        else st_coherent(&a.logits[(size_t)t * a.E + e], acc);
+      }
     }
   }
 }
