@@ -37,6 +37,7 @@
 #include <type_traits>
 
 #include "launch.hpp"
+#include "route_dev.hpp"
 
 namespace moe {
 
@@ -663,113 +664,28 @@ struct TopkArgs {
   float* __restrict__ w;
 };
 
-__device__ __forceinline__ uint32_t pf_sort_key(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float pf_key_value(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-
-// One wavefront per token: the same selection rule as the decode router
-// (k largest logits, ties to the lower id, softmax over them), written for
-// logits that a previous launch produced.
+// One wavefront per token: the selection of the small-M router (route_dev.hpp:
+// k largest logits, ties to the lower id, softmax over them) on logits that a
+// previous launch produced.
 __global__ __launch_bounds__(kBlock) void k_topk_rows(const TopkArgs a) {
-  __shared__ int lds_all[kWavesPerBlock][3 * kWave];
+  __shared__ __align__(16) int lds_all[kWavesPerBlock][3 * kMaxTopK];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * kWavesPerBlock + wave;
   if (t >= a.M) return;
-  int* lds = lds_all[wave];
-  constexpr int EPL = kMaxExperts / kWave;
-  uint32_t key[EPL];
-  bool present[EPL];
-  uint32_t lmax = 0;
+  uint32_t key[kTopkEPL];
+  bool present[kTopkEPL];
 #pragma unroll
-  for (int jj = 0; jj < EPL; ++jj) {
-    const int e = lane + kWave * jj;
-    present[jj] = e < a.E;
-    key[jj] = present[jj] ? pf_sort_key(a.logits[(size_t)t * a.E + e]) : 0u;
-    lmax = key[jj] > lmax ? key[jj] : lmax;
+  for (int j = 0; j < kTopkEPL; ++j) {
+    const int e = lane + kWave * j;
+    present[j] = e < a.E;
+    key[j] = present[j] ? sort_key(a.logits[(size_t)t * a.E + e]) : 0u;
   }
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  // the k-th largest lane maximum bounds the k-th largest key from below
-  uint32_t thr0 = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cb = thr0 | (1u << bit);
-    if (__popcll(__ballot(lmax >= cb)) >= a.k) thr0 = cb;
-  }
-  uint32_t cand = 0;
-  int C = 0;
-#pragma unroll
-  for (int jj = 0; jj < EPL; ++jj) {
-    const bool c = present[jj] && key[jj] >= thr0;
-    cand |= (uint32_t)c << jj;
-    C += __popcll(__ballot(c));
-  }
-  if (C > kWave) {  // exact selection of the k-th key, ties to the lower id
-    uint32_t thr = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cb = thr | (1u << bit);
-      int cnt = 0;
-#pragma unroll
-      for (int jj = 0; jj < EPL; ++jj) cnt += __popcll(__ballot(present[jj] && key[jj] >= cb));
-      if (cnt >= a.k) thr = cb;
-    }
-    int room = a.k;
-#pragma unroll
-    for (int jj = 0; jj < EPL; ++jj) room -= __popcll(__ballot(present[jj] && key[jj] > thr));
-    cand = 0;
-#pragma unroll
-    for (int jj = 0; jj < EPL; ++jj) {
-      const bool eq = present[jj] && key[jj] == thr;
-      const uint64_t eb = __ballot(eq);
-      const bool take = (present[jj] && key[jj] > thr) || (eq && __popcll(eb & lt) < room);
-      cand |= (uint32_t)take << jj;
-      room -= __popcll(eb);
-      if (room < 0) room = 0;
-    }
-    C = a.k;
-  }
-  uint32_t* lkey = reinterpret_cast<uint32_t*>(lds);
-  int* lid = lds + kWave;
-  int* lorder = lds + 2 * kWave;
-  int base = 0;
-#pragma unroll
-  for (int jj = 0; jj < EPL; ++jj) {
-    const bool c = (cand >> jj) & 1u;
-    const uint64_t bal = __ballot(c);
-    if (c) {
-      const int pos = base + __popcll(bal & lt);
-      lkey[pos] = key[jj];
-      lid[pos] = lane + kWave * jj;
-    }
-    base += __popcll(bal);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-  const uint32_t mk = lane < C ? lkey[lane] : 0u;
-  const int mi = lane < C ? lid[lane] : 0x7FFFFFFF;
-  int rank = 0;
-  for (int c = 0; c < C; ++c) {
-    const uint32_t ok = (uint32_t)__builtin_amdgcn_readlane((int)mk, c);
-    const int oi = __builtin_amdgcn_readlane(mi, c);
-    rank += (ok > mk || (ok == mk && oi < mi)) ? 1 : 0;
-  }
-  if (lane < C && rank < a.k) lorder[rank] = lane;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-  const int src = lane < a.k ? lorder[lane] : 0;
-  const uint32_t rk = __shfl(mk, src, 64);
-  const int ri = __shfl(mi, src, 64);
-  const float v = lane < a.k ? pf_key_value(rk) : 0.f;
-  const float vmax = __shfl(v, 0, 64);
-  const float ex = lane < a.k ? expf(v - vmax) : 0.f;
-  const float sum = wave_sum(ex);
+  int id;
+  float w;
+  topk_select(key, present, a.k, lane, lds_all[wave], id, w);
   if (lane < a.k) {
-    a.ids[(size_t)t * a.k + lane] = ri;
-    a.w[(size_t)t * a.k + lane] = ex / sum;
+    a.ids[(size_t)t * a.k + lane] = id;
+    a.w[(size_t)t * a.k + lane] = w;
   }
 }
 
