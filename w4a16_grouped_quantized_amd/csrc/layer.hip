@@ -273,10 +273,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     } else {
       const uint32_t ev = read_epoch(A);
       const int idx = blk - G.gSG, b = idx / a.KSgu, ks = idx % a.KSgu;
-      // the router rows' bytes and the key polls go first: this stream
-      // starts once every router key of this call has landed (it then runs
-      // under the top-k of the routed workgroups)
-      if (A.route) gather_keys(A, share_tag(ev, &tag_lds), dyn);
+      // this stream starts at once and runs under the routing (the router
+      // rows, the key hand-off and the top-k), which moves few bytes
       const int c0 = (ks * kWavesPerBlock + wave) * CWG;
       uint4 wc[CWG];
       const uint8_t* base = reinterpret_cast<const uint8_t*>(a.sh_gu) + ((size_t)(b * (a.H / 8) + c0) * kWave + lane) * 16;
@@ -437,9 +435,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const int row = tid % kDnRows, q = tid / kDnRows;
     const int row0 = r * kDnRows, tile = row0 >> 6, lrow = (row0 & 63) + row;
     constexpr int GKD = DG;  // I / 32
-    const uint32_t T = take_tag(A, ev, &tag_lds);
-    if (A.route) gather_keys(A, T, lkeys);
-    // the shared expert's rows, once the router's bytes are in
+    // the shared expert's rows, requested at once
     uint4 wsh[NSC > 0 ? NSC : 1];
     if constexpr (NSC > 0) {
 #pragma unroll
@@ -450,6 +446,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
                               : make_uint4(0, 0, 0, 0);
       }
     }
+    const uint32_t T = take_tag(A, ev, &tag_lds);
+    if (A.route) gather_keys(A, T, lkeys);
     select_slots(A, lkeys, topk_lds, lids, lw);
     if (!A.route && r == 0 && tid < a.S && !id_ok(lids[tid], a.E)) atomicOr(a.err, 1);
     const int nrec = a.k * GKD;  // (slot, group) records of one token, <= Q * NPQ
