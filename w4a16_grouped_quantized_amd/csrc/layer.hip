@@ -171,7 +171,8 @@ __device__ void gather_keys(const LayerArgs& A, uint32_t T, uint32_t* lkeys) {
 
 // ids and weights of every slot into lids / lw (LDS): the top-k of the keys
 // in lkeys (one wavefront per token), or the caller's.
-__device__ void select_slots(const LayerArgs& A, const uint32_t* lkeys, int* topk_lds, int* lids, float* lw) {
+__device__ void select_slots(const LayerArgs& A, const uint32_t* lkeys, int* topk_lds, int* lids, float* lw,
+                             bool want_w = true) {
   const ExpArgs& a = A.a;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   if (A.route) {
@@ -186,7 +187,7 @@ __device__ void select_slots(const LayerArgs& A, const uint32_t* lkeys, int* top
       }
       int id;
       float w;
-      topk_select(key, present, a.k, lane, topk_lds + wave * 3 * kMaxTopK, id, w);
+      topk_select(key, present, a.k, lane, topk_lds + wave * 3 * kMaxTopK, id, w, want_w);
       if (lane < a.k) {
         lids[t * a.k + lane] = id;
         lw[t * a.k + lane] = w;
@@ -343,7 +344,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         gbias[j] = gl.value();
       }
     if (A.route) gather_keys(A, T, lkeys);
-    select_slots(A, lkeys, topk_lds, lids, lw);
+    // the routed workgroups need the ids only, but the first one also hands
+    // the weights to the caller
+    select_slots(A, lkeys, topk_lds, lids, lw, idx == 0);
     // units: distinct valid experts in order of first occurrence (S <= 64);
     // the experts of one routed token are distinct: unit u is slot u
     if (wave == 0 && A.route && a.M == 1) {

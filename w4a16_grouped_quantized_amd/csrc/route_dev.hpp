@@ -59,10 +59,10 @@ __device__ __forceinline__ uint32_t kth_largest_lane_prefix(uint32_t key, int k)
 //     that order.
 // The selection itself on keys held in registers (key[j] of expert
 // lane + 64*j; absent entries are not present).  Lanes < k return the id and
-// softmax weight of rank `lane`.
+// softmax weight of rank `lane` (the weight only with want_w; 0 otherwise).
 constexpr int kTopkEPL = kMaxExperts / kWave;
 __device__ __forceinline__ void topk_select(const uint32_t (&key)[kTopkEPL], const bool (&present)[kTopkEPL], int k,
-                                            int lane, int* lds, int& out_id, float& out_w) {
+                                            int lane, int* lds, int& out_id, float& out_w, bool want_w = true) {
   constexpr int EPL = kTopkEPL;
   uint32_t lmax = 0;
 #pragma unroll
@@ -140,6 +140,11 @@ __device__ __forceinline__ void topk_select(const uint32_t (&key)[kTopkEPL], con
   const int src = lane < k ? lorder[lane] : 0;
   const uint32_t rk = lkey[src];
   const int ri = lid[src];
+  out_id = ri;
+  if (!want_w) {  // the ids alone
+    out_w = 0.f;
+    return;
+  }
   const float v = lane < k ? key_value(rk) : 0.f;
   const float vmax = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 0));
   const float ex = lane < k ? expf(v - vmax) : 0.f;
@@ -150,7 +155,6 @@ __device__ __forceinline__ void topk_select(const uint32_t (&key)[kTopkEPL], con
   } else {
     sum = wave_sum(ex);
   }
-  out_id = ri;
   out_w = ex / sum;
 }
 
