@@ -1,23 +1,29 @@
 #!/usr/bin/env python3
 """Benchmark of the W4A16 grouped-quantized MoE layer on one MI355X.
 
-Default workload (one "step" = one decode token through one Ling-shape MoE
+Headline workload (one "step" = one decode token through one Ling-shape MoE
 layer: route + gate_up/SiLU + down + weighted combine + shared expert, M = 1):
   hidden 2560, 512 routed experts, top-8, moe_intermediate 768, INT4 g32
   routed experts with bf16 scales, bf16 shared expert, fp32 router.
 Steps rotate over C resident copies of the layer (distinct device memory,
 distinct seeded routers), so a step never finds its weights in the 256 MB
-last-level cache; the step chain is captured once in a HIP graph and
-replayed.  Throughput is algorithmic bytes per step / time (GB/s) and
-microseconds per token.
+last-level cache; the step chain is captured in HIP graphs and replayed.
+Throughput is algorithmic bytes per step / time (GB/s) and microseconds per
+token.
 
-Other workloads (for measurement runs; the default is the one reported):
-  --workload verify2 / verify4   M = 2 / 4 tokens per step (speculative verify)
-  --workload stack               one token through 40 stacked layers with
-                                 RMSNorm between them (one step = 40 layers)
-  --workload prefill             one chunk of M = 4096 tokens per step (router
-                                 GEMM, grouped expert GEMMs on the matrix cores)
+Timing: W warm-up steps, then the K timed steps (exactly K) are replayed
+between HIP events on the launch stream, behind one untimed replay that keeps
+the GPU busy while the host enqueues them (so the region holds GPU work
+only); this is done three times and the median is reported, with each run's
+time beside it.
 
+The same run also measures, each with its own roofline (key "extra"): the
+speculative-verify steps (M = 2 and 4 tokens), one token through 40 stacked
+layers with RMSNorm between them, and one 4096-token prefill chunk; the HBM
+read rate a plain streaming kernel reaches on this part (the achievable
+ceiling); and the CPU oracle on this host's cores and on one core.
+
+--workload selects a different headline (then no extras are measured).
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -25,6 +31,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -34,6 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
 
 # Algorithmic bytes (Ling shape): every weight byte a step must read once,
 # plus activations in and out.
@@ -44,260 +52,365 @@ SHARED_GU_BYTES = 2 * 768 * 2560 * 2                                    # 7,864,
 SHARED_DN_BYTES = 2560 * 768 * 2                                        # 3,932,160
 ROUTER_BYTES = 512 * 2560 * 4                                           # 5,242,880
 TOKEN_IO_BYTES = 2 * 2560 * 2                                           # x in, out back
-
+STACK_LAYERS = 40
 
 WORKLOAD_NAMES = {"decode": "ling_moe_layer_decode_m1", "verify2": "ling_moe_layer_verify_m2",
                   "verify4": "ling_moe_layer_verify_m4", "stack": "ling_moe_stack40_decode_m1",
                   "prefill": "ling_moe_layer_prefill_m4096"}
+TOKENS = {"decode": 1, "verify2": 2, "verify4": 4, "stack": 1, "prefill": 4096}
+# (timed steps, warm-up steps) of the extra workloads measured beside the headline
+EXTRA_STEPS = {"verify2": (256, 32), "verify4": (256, 32), "stack": (16, 4), "prefill": (8, 2)}
 
 
 def step_bytes(n_unique_experts: int, M: int) -> int:
     return n_unique_experts * EXPERT_BYTES + SHARED_GU_BYTES + SHARED_DN_BYTES + ROUTER_BYTES + M * TOKEN_IO_BYTES
 
 
-def parse():
+def prefill_flops(M: int, k: int = 8) -> float:
+    """Expert flops of one chunk: routed pairs and the shared expert, gate_up
+    (2 x 768 x 2560) and down (2560 x 768) multiply-adds each."""
+    per = 2 * 768 * 2560 + 2560 * 768
+    return 2.0 * M * k * per + 2.0 * M * per
+
+
+def parse(argv=None):
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=4096)
-    p.add_argument("--warmup", type=int, default=512)
-    p.add_argument("--workload", default="decode", choices=["decode", "verify2", "verify4", "stack", "prefill"])
-    p.add_argument("--copies", type=int, default=None,
-                   help="resident layer copies to rotate over (default 32; 1 for prefill, which reads every expert)")
-    p.add_argument("--chunk", type=int, default=256, help="steps captured per graph")
+    p.add_argument("--steps", type=int, default=2048)
+    p.add_argument("--warmup", type=int, default=256)
+    p.add_argument("--workload", default="decode", choices=list(WORKLOAD_NAMES))
+    p.add_argument("--copies", type=int, default=32,
+                   help="resident layer copies the decode/verify steps rotate over (prefill uses one)")
+    p.add_argument("--chunk", type=int, default=256, help="decode/verify steps captured per graph")
+    p.add_argument("--runs", type=int, default=3, help="timed runs of K steps; the median is reported")
     p.add_argument("--path", default="layer", choices=["layer", "calls"],
-                   help="layer: one moe_layer_w4a16 call per layer step (one launch at small M); "
+                   help="layer: one moe_layer_w4a16 call per layer step (one launch at M = 1); "
                         "calls: moe_route then moe_forward_w4a16")
+    p.add_argument("--no-extras", action="store_true", help="measure the headline workload only")
     p.add_argument("--cpu-baseline-seconds", type=float, default=12.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--stage-steps", type=int, default=256, help="eager steps timed per stage")
+    p.add_argument("--stage-steps", type=int, default=256, help="launches per graph when timing one entry point")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="after timing, run a plain device copy of this many MiB (reference for HBM byte counters)")
-    return p.parse_args()
+    return p.parse_args(argv)
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def main():
-    args = parse()
+class Ctx:
+    """Device state shared by the workloads of one run."""
+
+    def __init__(self, args, n_copies):
+        import torch
+
+        from w4a16_grouped_quantized_amd import binding as B
+        from w4a16_grouped_quantized_amd import synth
+        self.torch, self.B, self.synth, self.args = torch, B, synth, args
+        self.shape = synth.LING
+        self.cfg = B.config(self.shape)
+        t0 = time.time()
+        self.layer = synth.make_layer(self.shape, 1, threads=16)
+        base = B.MoeLayer(self.layer)
+        log(f"layer generated and packed in {time.time() - t0:.1f}s; build: {B.build_info()}")
+        # copies: distinct device memory; distinct seeded routers (layer seeds 1000 + c)
+        self.copies = []
+        for c in range(n_copies):
+            packed = base.packed if c == 0 else base.packed.clone()
+            router = torch.from_numpy(synth.make_router(self.shape, 1000 + c)).cuda()
+            self.copies.append((packed, router))
+        torch.cuda.synchronize()
+        log(f"{n_copies} resident copies ({n_copies * (base.packed.numel() + ROUTER_BYTES) / 1e9:.1f} GB)")
+        self.stream = torch.cuda.current_stream()
+        self.ws = {}
+
+    def workspace(self, M):
+        if M not in self.ws:
+            self.ws[M] = self.B.Workspace(self.cfg, M)
+        return self.ws[M]
+
+    def event(self):
+        return self.torch.cuda.Event(enable_timing=True)
+
+
+def time_graph_region(ctx, graphs, runs):
+    """Median over `runs` of the GPU time of replaying `graphs` (a list of
+    (graph, times)) back to back, each run behind one untimed replay of the
+    first graph so that the region holds GPU work only.  Returns (median ms,
+    list of run ms)."""
+    torch = ctx.torch
+    res = []
+    for _ in range(runs):
+        graphs[0][0].replay()            # keeps the GPU busy while the region is enqueued
+        e0, e1 = ctx.event(), ctx.event()
+        e0.record(ctx.stream)
+        for g, n in graphs:
+            for _ in range(n):
+                g.replay()
+        e1.record(ctx.stream)
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1))
+    return float(np.median(res)), res
+
+
+def measure_steps(ctx, workload, K, W, path):
+    """decode / verify / stack: K timed steps replayed from graphs (after W
+    warm-up steps); returns the workload's result dict."""
+    torch, B, synth, shape, cfg = ctx.torch, ctx.B, ctx.synth, ctx.shape, ctx.cfg
+    M = TOKENS[workload]
+    stack = workload == "stack"
+    n_layers = STACK_LAYERS if stack else min(ctx.args.copies, len(ctx.copies))
+    chunk = max(1, min(8 if stack else ctx.args.chunk, K))
+    ws = ctx.workspace(M)
+    X = torch.from_numpy(synth.make_tokens(shape, 2, chunk * M).view(np.int16)).view(torch.bfloat16).cuda()
+    ids = torch.empty((chunk, M, shape.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((chunk, M, shape.top_k), dtype=torch.float32, device="cuda")
+    out = torch.empty((chunk, M, shape.hidden), dtype=torch.bfloat16, device="cuda")
+    out2 = torch.empty_like(out)
+    xn = torch.empty_like(out)
+
+    def step(i, s):
+        x_in = X[i * M:(i + 1) * M]
+        if stack:
+            for l in range(n_layers):
+                pk, rt = ctx.copies[l]
+                bufs = (out[i], out2[i])     # layer l reads layer l-1's output
+                if path == "layer":
+                    if l == 0:
+                        B.layer(cfg, rt, pk, x_in, ids[i], w[i], bufs[0], ws.buf)
+                    else:
+                        B.layer(cfg, rt, pk, bufs[(l - 1) % 2], ids[i], w[i], bufs[l % 2], ws.buf,
+                                flags=B.MOE_F_INPUT_RMSNORM, x_norm=xn[i])
+                elif l == 0:
+                    B.route(cfg, rt, x_in, ids[i], w[i], ws.buf)
+                    B.forward(cfg, pk, x_in, ids[i], w[i], bufs[0], ws.buf)
+                else:
+                    B.route(cfg, rt, bufs[(l - 1) % 2], ids[i], w[i], ws.buf, flags=B.MOE_F_INPUT_RMSNORM,
+                            x_norm=xn[i])
+                    B.forward(cfg, pk, xn[i], ids[i], w[i], bufs[l % 2], ws.buf)
+        else:
+            pk, rt = ctx.copies[s % n_layers]
+            if path == "layer":
+                B.layer(cfg, rt, pk, x_in, ids[i], w[i], out[i], ws.buf)
+            else:
+                B.route(cfg, rt, x_in, ids[i], w[i], ws.buf)
+                B.forward(cfg, pk, x_in, ids[i], w[i], out[i], ws.buf)
+
+    # exactly W warm-up steps, eager
+    for s in range(W):
+        step(s % chunk, s)
+    torch.cuda.synchronize()
+
+    def capture(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                step(i, i)
+        return g
+
+    g = capture(chunk)
+    graphs = [(g, K // chunk)]
+    if K % chunk:
+        graphs.append((capture(K % chunk), 1))
+    ms, runs = time_graph_region(ctx, graphs, ctx.args.runs)
+    ms_per_step = ms / K
+    ids_np = ids.cpu().numpy()
+    if stack:
+        uniq = 8.0
+        bytes_per_step = float(n_layers * step_bytes(8, 1))
+    else:
+        u = [len(np.unique(ids_np[i])) for i in range(chunk)]
+        uniq = float(np.mean(u))
+        bytes_per_step = float(np.mean([step_bytes(n, M) for n in u]))
+    gbs = bytes_per_step / (ms_per_step * 1e-3) / 1e9
+    per_token = ms_per_step * 1e3 / (n_layers if stack else M)
+    log(f"{workload}: {K} steps, runs {', '.join(f'{r:.3f}' for r in runs)} ms: {ms_per_step * 1e3:.2f} us/step, "
+        f"{gbs:.0f} GB/s, unique experts/step {uniq:.2f}")
+    return {"workload": WORKLOAD_NAMES[workload], "tokens_per_step": M, "steps": K, "warmup": W,
+            "ms_per_step": ms_per_step, "run_ms": [round(r, 4) for r in runs], "gbs": gbs,
+            "us_per_token": per_token, "bytes_per_step": bytes_per_step, "unique_experts_per_step": uniq,
+            "resident_layer_copies": n_layers, "graph_steps_per_replay": chunk,
+            "_buffers": (X, ids, w, out, ws)}
+
+
+def stage_times(ctx, M, bufs, n_layers):
+    """Per-launch duration of each small-M entry point on its own: a graph of n
+    back-to-back launches over the same rotation of layer copies, replayed
+    between HIP events on the launch stream; duration = elapsed / n."""
+    torch, B, cfg = ctx.torch, ctx.B, ctx.cfg
+    X, ids, w, out, ws = bufs
+    chunk = ids.shape[0]
+    out2 = torch.empty_like(out)
+    n = max(chunk, ctx.args.stage_steps)
+    names = ("route", "forward", "gate_up", "down")
+    res = {}
+    for stage, nm in enumerate(names):
+        gs = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gs):
+            for i in range(n):
+                pk, rt = ctx.copies[i % n_layers]
+                j = i % chunk
+                x_in = X[j * M:(j + 1) * M]
+                if stage == 0:
+                    B.route(cfg, rt, x_in, ids[j], w[j], ws.buf)
+                elif stage == 1:
+                    B.forward(cfg, pk, x_in, ids[j], w[j], out2[j], ws.buf)
+                elif stage == 2:
+                    B.gate_up(cfg, pk, x_in, ids[j], ws.buf)
+                else:
+                    B.down(cfg, pk, ids[j], w[j], out2[j], ws.buf)
+        gs.replay()
+        torch.cuda.synchronize()
+        ms, _ = time_graph_region(ctx, [(gs, 4)], 1)
+        res[nm] = round(ms * 1e3 / (4 * n), 3)
+        del gs
+    return res
+
+
+def roofline_steps(ctx, r, path):
+    """Roofline of the dominant kernel of a decode/verify/stack measurement."""
+    M = r["tokens_per_step"]
+    stack = r["workload"] == WORKLOAD_NAMES["stack"]
+    one_launch = path == "layer" and M == 1
+    if one_launch:
+        # k_layer is the only kernel, one launch per layer step
+        launches = STACK_LAYERS if stack else 1
+        us = r["ms_per_step"] * 1e3 / launches
+        nbytes = r["bytes_per_step"] / launches
+        kernel = "k_layer (one launch per layer: router, top-k, shared and routed experts, output)"
+    else:
+        # separate kernels; the dominant one is k_gate_up: the gate_up weights of
+        # the step's distinct experts and of the shared expert, and the token rows
+        us = r["stage_us"]["gate_up"]
+        nbytes = r["unique_experts_per_step"] * EXPERT_GU_BYTES + SHARED_GU_BYTES + M * 2560 * 2
+        kernel = "k_gate_up (routed INT4 gate_up + SiLU of the step's distinct experts, shared gate_up)"
+    achieved = nbytes / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": measured_traffic(r["workload"]) if one_launch else None,
+            "bytes_per_launch": int(nbytes), "us_per_launch": round(us, 3)}
+
+
+def measure_prefill(ctx, K, W):
+    """One 4096-token chunk per step: route (router GEMM + top-k) and forward
+    (permutation, grouped GEMMs, combine), each timed eagerly between HIP
+    events on the launch stream; and the whole step replayed from a graph."""
+    torch, B, synth, shape, cfg = ctx.torch, ctx.B, ctx.synth, ctx.shape, ctx.cfg
+    M = TOKENS["prefill"]
+    ws = ctx.workspace(M)
+    pk, rt = ctx.copies[0]
+    X = torch.from_numpy(synth.make_tokens(shape, 2, M).view(np.int16)).view(torch.bfloat16).cuda()
+    ids = torch.empty((M, shape.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((M, shape.top_k), dtype=torch.float32, device="cuda")
+    out = torch.empty((M, shape.hidden), dtype=torch.bfloat16, device="cuda")
+    for _ in range(W):
+        B.route(cfg, rt, X, ids, w, ws.buf)
+        B.forward(cfg, pk, X, ids, w, out, ws.buf)
+    torch.cuda.synchronize()
+    ev = [[ctx.event() for _ in range(3)] for _ in range(K)]
+    for e in ev:
+        e[0].record(ctx.stream)
+        B.route(cfg, rt, X, ids, w, ws.buf)
+        e[1].record(ctx.stream)
+        B.forward(cfg, pk, X, ids, w, out, ws.buf)
+        e[2].record(ctx.stream)
+    torch.cuda.synchronize()
+    t = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])] for e in ev]) * 1e3
+    med = np.median(t, axis=0)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.route(cfg, rt, X, ids, w, ws.buf)
+        B.forward(cfg, pk, X, ids, w, out, ws.buf)
+    ms, runs = time_graph_region(ctx, [(g, K)], ctx.args.runs)
+    ms_per_step = ms / K
+    nbytes = 512 * EXPERT_BYTES + SHARED_GU_BYTES + SHARED_DN_BYTES + ROUTER_BYTES + M * TOKEN_IO_BYTES
+    flops = prefill_flops(M)
+    tflops = flops / (med[1] * 1e-6) / 1e12
+    log(f"prefill: route {med[0]:.1f} us, forward {med[1]:.1f} us (eager medians); graph {ms_per_step * 1e3:.1f} us/chunk")
+    return {"workload": WORKLOAD_NAMES["prefill"], "tokens_per_step": M, "steps": K, "warmup": W,
+            "ms_per_step": ms_per_step, "run_ms": [round(r, 4) for r in runs],
+            "gbs": nbytes / (ms_per_step * 1e-3) / 1e9, "us_per_token": ms_per_step * 1e3 / M,
+            "bytes_per_step": float(nbytes),
+            "stage_us": {"route": round(float(med[0]), 3), "forward": round(float(med[1]), 3)},
+            "roofline": {"bound": "mfma", "kernel": "moe_forward_w4a16 at M=4096 (grouped GEMM kernels + permutation "
+                                                      "+ combine)", "achieved": round(tflops, 2),
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                         "traffic": measured_traffic(WORKLOAD_NAMES["prefill"]), "flops_per_launch": flops}}
+
+
+def read_ceiling(ctx, gib=2, runs=5):
+    """GB/s of the plain streaming read (moe_probe_read) over a buffer far
+    larger than the last-level cache: median of `runs`."""
+    torch, B = ctx.torch, ctx.B
+    n = gib << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(3)
+    blocks = 4096
+    sink = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+    B.probe_read(buf, sink, blocks)
+    torch.cuda.synchronize()
+    res = []
+    for _ in range(runs):
+        e0, e1 = ctx.event(), ctx.event()
+        e0.record(ctx.stream)
+        B.probe_read(buf, sink, blocks)
+        e1.record(ctx.stream)
+        torch.cuda.synchronize()
+        res.append(n / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del buf
+    gbs = float(np.median(res))
+    log(f"read ceiling: {gbs:.0f} GB/s ({gib} GiB, 16-byte loads, {blocks} workgroups; runs "
+        f"{', '.join(f'{r:.0f}' for r in res)})")
+    return {"gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4), "bytes": n,
+            "kernel": "moe_probe_read (grid-stride 16-byte loads, every byte once)"}
+
+
+def summary(r, ceiling):
+    d = {k: v for k, v in r.items() if not k.startswith("_")}
+    for k in ("ms_per_step", "gbs", "us_per_token"):
+        d[k] = round(d[k], 6 if k == "ms_per_step" else 3)
+    if ceiling and d.get("roofline", {}).get("unit") == "GB/s":
+        d["roofline"]["frac_of_read_ceiling"] = round(d["roofline"]["achieved"] / ceiling["gbs"], 4)
+    return d
+
+
+def main(argv=None):
+    args = parse(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(expert and tensor sharding are design notes only); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
-
-    from w4a16_grouped_quantized_amd import binding as B
-    from w4a16_grouped_quantized_amd import synth
-
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    from w4a16_grouped_quantized_amd import binding as B
     B.lib()
-    shape = synth.LING
-    cfg = B.config(shape)
-    M = {"decode": 1, "verify2": 2, "verify4": 4, "stack": 1, "prefill": 4096}[args.workload]
-    prefill = args.workload == "prefill"
-    if args.copies is None:
-        args.copies = 1 if prefill else 32
-    if prefill:
-        args.chunk = min(args.chunk, 4)
-    n_layers = 40 if args.workload == "stack" else args.copies
 
-    t0 = time.time()
-    layer = synth.make_layer(shape, 1, threads=16)
-    base = B.MoeLayer(layer)
-    log(f"layer generated and packed in {time.time() - t0:.1f}s; build: {B.build_info()}")
+    head = args.workload
+    extras = [] if (args.no_extras or head != "decode") else ["verify2", "verify4", "stack", "prefill"]
+    need = 1 if head == "prefill" else args.copies
+    if head == "stack" or "stack" in extras:
+        need = max(need, STACK_LAYERS)
+    ctx = Ctx(args, need)
 
-    # C copies: distinct device memory; distinct seeded routers (layer seeds 1000 + c).
-    copies = []
-    for c in range(n_layers):
-        packed = base.packed if c == 0 else base.packed.clone()
-        router = torch.from_numpy(synth.make_router(shape, 1000 + c)).cuda()
-        copies.append((packed, router))
-    torch.cuda.synchronize()
-    log(f"{n_layers} resident copies ({n_layers * (base.packed.numel() + 5242880) / 1e9:.1f} GB)")
+    results = {}
+    for wl in [head] + extras:
+        K, W = (args.steps, args.warmup) if wl == head else EXTRA_STEPS[wl]
+        if wl == "prefill":
+            results[wl] = measure_prefill(ctx, K, W)
+            continue
+        r = measure_steps(ctx, wl, K, W, args.path)
+        if TOKENS[wl] > 1 or args.path == "calls" or wl == head:
+            r["stage_us"] = stage_times(ctx, TOKENS[wl], r["_buffers"], min(args.copies, len(ctx.copies)))
+            log(f"{wl}: entry point us per launch (graphs of back-to-back launches): " +
+                " ".join(f"{k} {v:.2f}" for k, v in r["stage_us"].items()))
+        r["roofline"] = roofline_steps(ctx, r, args.path)
+        results[wl] = r
 
-    ws = B.Workspace(cfg, max(M, 1))
-    stream = torch.cuda.current_stream()
-    chunk = max(1, min(args.chunk, args.steps))
-    n_tok = chunk * M
-    X = torch.from_numpy(synth.make_tokens(shape, 2, n_tok).view(np.int16)).view(torch.bfloat16).cuda()
-    ids = torch.empty((chunk, M, shape.top_k), dtype=torch.int32, device="cuda")
-    w = torch.empty((chunk, M, shape.top_k), dtype=torch.float32, device="cuda")
-    out = torch.empty((chunk, M, shape.hidden), dtype=torch.bfloat16, device="cuda")
-    xn = torch.empty((chunk, M, shape.hidden), dtype=torch.bfloat16, device="cuda")
-    out2 = torch.empty((chunk, M, shape.hidden), dtype=torch.bfloat16, device="cuda")
-
-    def run_steps(lo, hi, step_offset):
-        """Enqueue steps lo..hi-1 (the graph body)."""
-        for i in range(lo, hi):
-            s = step_offset + i
-            if args.workload == "stack":
-                # one token through all layers; layer l reads the previous output
-                x_in = X[i * M:(i + 1) * M]
-                for l in range(n_layers):
-                    pk, rt = copies[l]
-                    if args.path == "layer":
-                        # outputs alternate between two buffers: layer l reads layer l-1's
-                        bufs = (out[i], out2[i])
-                        if l == 0:
-                            B.layer(cfg, rt, pk, x_in, ids[i], w[i], bufs[0], ws.buf)
-                        else:
-                            B.layer(cfg, rt, pk, bufs[(l - 1) % 2], ids[i], w[i], bufs[l % 2], ws.buf,
-                                    flags=B.MOE_F_INPUT_RMSNORM, x_norm=xn[i])
-                    elif l == 0:
-                        B.route(cfg, rt, x_in, ids[i], w[i], ws.buf)
-                        B.forward(cfg, pk, x_in, ids[i], w[i], out[i], ws.buf)
-                    else:
-                        B.route(cfg, rt, out[i], ids[i], w[i], ws.buf, flags=B.MOE_F_INPUT_RMSNORM, x_norm=xn[i])
-                        B.forward(cfg, pk, xn[i], ids[i], w[i], out[i], ws.buf)
-            else:
-                pk, rt = copies[s % n_layers]
-                x_in = X[i * M:(i + 1) * M]
-                if args.path == "layer":
-                    B.layer(cfg, rt, pk, x_in, ids[i], w[i], out[i], ws.buf)
-                else:
-                    B.route(cfg, rt, x_in, ids[i], w[i], ws.buf)
-                    B.forward(cfg, pk, x_in, ids[i], w[i], out[i], ws.buf)
-
-    # warm the stream outside capture, then capture one chunk
-    run_steps(0, chunk, 0)
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        run_steps(0, chunk, 0)
-    reps = max(1, args.steps // chunk)
-    steps = reps * chunk
-    wreps = max(1, args.warmup // chunk)
-    for _ in range(wreps):
-        g.replay()
-    torch.cuda.synchronize()
-
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    tw = time.perf_counter()
-    e0.record(stream)
-    for _ in range(reps):
-        g.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - tw
-    ms = e0.elapsed_time(e1)
-    ms_per_step = ms / steps
-
-    ids_np = ids.cpu().numpy()
-    if args.workload == "stack":
-        uniq = 8.0  # per layer at M = 1
-        bytes_per_step = n_layers * step_bytes(8, 1)
-    else:
-        uniq = float(np.mean([len(np.unique(ids_np[i])) for i in range(chunk)]))
-        bytes_per_step = float(np.mean([step_bytes(len(np.unique(ids_np[i])), M) for i in range(chunk)]))
-    gbs = bytes_per_step / (ms_per_step * 1e-3) / 1e9
-    log(f"{steps} steps in {ms:.2f} ms (wall {wall * 1e3:.2f} ms): {ms_per_step * 1e3:.2f} us/step, "
-        f"{gbs:.0f} GB/s, unique experts/step {uniq:.2f}")
-
-    one_launch = False
-    if prefill:
-        # route (router GEMM + top-k) and forward (permutation, grouped GEMMs,
-        # combine) timed separately, eager, HIP events on the launch stream
-        def time_calls(n):
-            ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
-            for i in range(n):
-                pk, rt = copies[i % n_layers]
-                j = i % chunk
-                x_in = X[j * M:(j + 1) * M]
-                e = ev[i]
-                e[0].record(stream)
-                B.route(cfg, rt, x_in, ids[j], w[j], ws.buf)
-                e[1].record(stream)
-                B.forward(cfg, pk, x_in, ids[j], w[j], out[j], ws.buf)
-                e[2].record(stream)
-            torch.cuda.synchronize()
-            r = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2])] for e in ev]) * 1e3
-            return np.median(r, axis=0), np.mean(r, axis=0)
-
-        time_calls(2)
-        st_med, st_mean = time_calls(max(4, min(args.stage_steps, 16)))
-        log(f"call us (median) route {st_med[0]:.1f} forward {st_med[1]:.1f}; (mean) {st_mean[0]:.1f} {st_mean[1]:.1f}")
-        pairs = M * shape.top_k
-        flops = 2.0 * pairs * (2 * 768 * 2560 + 2560 * 768) + 2.0 * M * (2 * 768 * 2560 + 2560 * 768)
-        tflops = flops / (st_mean[1] * 1e-6) / 1e12
-        stage = {"route": round(float(st_mean[0]), 3), "forward": round(float(st_mean[1]), 3)}
-        roof = {"bound": "mfma", "kernel": "moe_forward_w4a16 at M=4096 (grouped GEMM kernels + permutation + combine)",
-                "achieved": round(tflops, 2), "peak": 2500.0, "unit": "TFLOP/s", "frac": round(tflops / 2500.0, 4),
-                "traffic": None, "flops_per_launch": flops}
-    else:
-        # Per-entry-point durations, each a graph of n back-to-back launches of
-        # that call alone over the same rotation of layer copies, replayed
-        # between HIP events on the launch stream; duration per launch =
-        # elapsed / n.  route = moe_route (k_route), forward = moe_forward_w4a16
-        # on the routed ids (k_gate_up then k_down), and those two kernels
-        # alone.
-        stage_names = ("route", "forward", "gate_up", "down")
-
-        def stage_graph(stage, n):
-            gs = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gs):
-                for i in range(n):
-                    pk, rt = copies[i % n_layers]
-                    j = i % chunk
-                    x_in = X[j * M:(j + 1) * M]
-                    if stage == 0:
-                        B.route(cfg, rt, x_in, ids[j], w[j], ws.buf)
-                    elif stage == 1:
-                        B.forward(cfg, pk, x_in, ids[j], w[j], out2[j], ws.buf)
-                    elif stage == 2:
-                        B.gate_up(cfg, pk, x_in, ids[j], ws.buf)
-                    else:
-                        B.down(cfg, pk, ids[j], w[j], out2[j], ws.buf)
-            return gs
-
-        def time_stages(n):
-            res = []
-            for stage in range(len(stage_names)):
-                gs = stage_graph(stage, n)
-                gs.replay()
-                torch.cuda.synchronize()
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                reps_s = 4
-                e0.record(stream)
-                for _ in range(reps_s):
-                    gs.replay()
-                e1.record(stream)
-                torch.cuda.synchronize()
-                res.append(e0.elapsed_time(e1) * 1e3 / (reps_s * n))
-                del gs
-            return np.array(res)
-
-        st = time_stages(max(chunk, args.stage_steps))
-        log("entry point us per launch (graph of back-to-back launches): " +
-            " ".join(f"{nm} {v:.2f}" for nm, v in zip(stage_names, st)))
-        stage = {nm: round(float(v), 3) for nm, v in zip(stage_names, st)}
-        n_uniq = uniq if args.workload != "stack" else 8
-        one_launch = args.path == "layer" and M == 1
-        if one_launch:
-            # the dominant kernel is the only one: k_layer, one launch per
-            # layer; its duration per launch is the timed region / launches
-            launches = n_layers if args.workload == "stack" else 1
-            us_launch = ms_per_step * 1e3 / launches
-            bytes_launch = bytes_per_step / launches
-            kernel = "k_layer (one launch per layer: router, top-k, shared and routed experts, output)"
-        else:
-            # separate kernels (k_route, k_gate_up, k_down); the dominant one
-            # is k_gate_up: the gate_up weights of the step's distinct experts
-            # and of the shared expert, and the step's token rows
-            us_launch = float(st[2])
-            bytes_launch = n_uniq * EXPERT_GU_BYTES + SHARED_GU_BYTES + M * 2560 * 2
-            kernel = "k_gate_up (routed INT4 gate_up + SiLU of the step's distinct experts, shared gate_up)"
-        achieved = bytes_launch / (us_launch * 1e-6) / 1e9
-        roof = {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                "bytes_per_launch": int(bytes_launch), "us_per_launch": round(us_launch, 3)}
+    ceiling = read_ceiling(ctx)
 
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib << 20
@@ -309,40 +422,41 @@ def main():
         del src, dst
         log(f"calibration copy: {args.calib_copy_mib} MiB x 2")
 
-    if roof.get("traffic") is None:
-        roof["traffic"] = measured_traffic(WORKLOAD_NAMES[args.workload]) if one_launch or prefill else None
-
     cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(shape, layer, args.cpu_baseline_seconds)
+    if not args.no_cpu_baseline and head in ("decode", "verify2", "verify4", "stack"):
+        cpu = cpu_baseline(ctx.shape, ctx.layer, args.cpu_baseline_seconds)
 
-    dtype = "bf16 activations, int4 weights, fp32 accumulate"
+    h = summary(results[head], ceiling)
     line = {
         "metric": "MoE layer us/token and achieved HBM GB/s at batch 1 (W4A16 g32, top-8 of 512)",
-        "value": round(gbs, 1),
+        "value": round(h["gbs"], 1),
         "unit": "GB/s",
-        # per token per layer
-        "us_per_token": round(ms_per_step * 1e3 / (M if args.workload != "stack" else n_layers), 3),
+        "us_per_token": h["us_per_token"],
         "n_gpus": 1,
-        "steps": steps,
-        "warmup": wreps * chunk,
-        "ms_per_step": round(ms_per_step, 6),
+        "steps": h["steps"],
+        "warmup": h["warmup"],
+        "ms_per_step": h["ms_per_step"],
+        "run_ms": h["run_ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": WORKLOAD_NAMES[args.workload],
+            "workload": h["workload"],
             "hidden": 2560, "n_experts": 512, "top_k": 8, "moe_intermediate": 768, "group_size": 32,
-            "tokens_per_step": M, "resident_layer_copies": n_layers, "graph_steps_per_replay": chunk,
-            "algorithmic_bytes_per_step": int(bytes_per_step), "unique_experts_per_step": uniq,
-            "compute": dtype,
+            "tokens_per_step": h["tokens_per_step"], "resident_layer_copies": h.get("resident_layer_copies", 1),
+            "graph_steps_per_replay": h.get("graph_steps_per_replay", 1), "timed_runs": args.runs,
+            "algorithmic_bytes_per_step": int(h["bytes_per_step"]),
+            "unique_experts_per_step": h.get("unique_experts_per_step", 512.0),
+            "compute": "bf16 activations, int4 weights, fp32 accumulate",
         },
-        "stage_us": stage,
-        "roofline": roof,
+        "stage_us": h.get("stage_us"),
+        "roofline": h["roofline"],
+        "read_ceiling": ceiling,
         "cpu_baseline": cpu,
-        "build": B.build_info(),
+        "extra": {wl: summary(results[wl], ceiling) for wl in extras},
+        "build": ctx.B.build_info(),
     }
     print(json.dumps(line), flush=True)
 
@@ -381,15 +495,10 @@ def measured_traffic(workload: str):
         return None
 
 
-def cpu_baseline(shape, layer, seconds):
-    """The oracle (fp64, plain loops) on host cores: route + forward for as
-    many decode tokens of the same layer as fit in about `seconds`."""
+def oracle_tokens_per_time(shape, layer, x, seconds):
+    """Route + forward of single decode tokens through the oracle for about
+    `seconds` (after one warm-up token); returns (tokens, elapsed s)."""
     from oracle import oracle as O
-    O.lib()
-    threads = O.num_threads()
-    from w4a16_grouped_quantized_amd import synth
-    x = synth.make_tokens(shape, 2, 4096)
-    # warm-up token
     ids, w, _, _ = O.route(shape, layer.router_w, x[:1])
     O.forward(shape, layer, x[:1], ids, w)
     n = 0
@@ -399,13 +508,56 @@ def cpu_baseline(shape, layer, seconds):
         ids, w, _, _ = O.route(shape, layer.router_w, xt)
         O.forward(shape, layer, xt, ids, w)
         n += 1
-    dt = time.perf_counter() - t0
+    return n, time.perf_counter() - t0
+
+
+def cpu_baseline(shape, layer, seconds):
+    """The oracle (fp64, plain loops) on the host: route + forward for as many
+    decode tokens of the same layer as fit in about `seconds`, on all of the
+    threads OpenMP gives it here, and again in a child process on one thread."""
+    from oracle import oracle as O
+    from w4a16_grouped_quantized_amd import synth
+    O.lib()
+    threads = O.num_threads()
+    x = synth.make_tokens(shape, 2, 4096)
+    n, dt = oracle_tokens_per_time(shape, layer, x, seconds)
     us = dt / n * 1e6
-    gbs = step_bytes(8, 1) / (us * 1e-6) / 1e9
     log(f"cpu baseline (oracle): {n} tokens in {dt:.1f}s, {us:.0f} us/token, {threads} threads")
-    return {"value": round(gbs, 4), "unit": "GB/s", "us_per_token": round(us, 1), "cores": threads,
-            "kind": "oracle", "sample": f"{n} decode tokens (M=1) of the seed-1 Ling-shape layer, route + forward"}
+    one = None
+    try:
+        env = dict(os.environ, OMP_NUM_THREADS="1")
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-one-core", str(seconds / 2)],
+                           env=env, capture_output=True, text=True, timeout=600)
+        if r.returncode == 0:
+            one = json.loads(r.stdout.strip().splitlines()[-1])
+            log(f"cpu baseline (oracle, 1 thread): {one['tokens']} tokens, {one['us_per_token']:.0f} us/token")
+        else:
+            log(f"one-thread oracle run failed: {r.stderr[-300:]}")
+    except (subprocess.SubprocessError, ValueError) as e:
+        log(f"one-thread oracle run failed: {e}")
+    res = {"value": round(step_bytes(8, 1) / (us * 1e-6) / 1e9, 4), "unit": "GB/s", "us_per_token": round(us, 1),
+           "cores": threads, "kind": "oracle",
+           "sample": f"{n} decode tokens (M=1) of the seed-1 Ling-shape layer, route + forward"}
+    if one:
+        res["one_core"] = {"value": round(step_bytes(8, 1) / (one["us_per_token"] * 1e-6) / 1e9, 4), "unit": "GB/s",
+                           "us_per_token": round(one["us_per_token"], 1), "cores": 1,
+                           "sample": f"{one['tokens']} decode tokens, same layer"}
+    return res
+
+
+def oracle_one_core(seconds):
+    """Child process of cpu_baseline: the oracle with OMP_NUM_THREADS=1."""
+    from oracle import oracle as O
+    from w4a16_grouped_quantized_amd import synth
+    O.lib()
+    layer = synth.make_layer(synth.LING, 1, threads=16)
+    x = synth.make_tokens(synth.LING, 2, 4096)
+    n, dt = oracle_tokens_per_time(synth.LING, layer, x, seconds)
+    print(json.dumps({"tokens": n, "us_per_token": dt / n * 1e6, "threads": O.num_threads()}), flush=True)
 
 
 if __name__ == "__main__":
-    main()
+    if len(sys.argv) == 3 and sys.argv[1] == "--oracle-one-core":
+        oracle_one_core(float(sys.argv[2]))
+    else:
+        main()

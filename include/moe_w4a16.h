@@ -85,18 +85,30 @@ typedef struct {
 } moe_weights_plain;
 
 /* Bytes of the device layout produced by moe_pack_weights (routed + shared
- * experts; the router is not part of it).  0 on an invalid config. */
+ * experts; the router is not part of it).  0 on an invalid config.
+ * The routed experts are the symmetric 4-bit, group-32 part of the int4
+ * checkpoint and the shared expert its BF16 part (vLLM recipe page
+ * "inclusionAI/Ling-3.0-flash", "Single-GPU int4"). */
 size_t moe_packed_size(const moe_config* cfg /* host */);
 
 /* Rearrange plain weights into the library's device layout (same bytes,
  * tiled so that every 16-byte load of a wavefront is contiguous and one
- * lane owns one weight row).  One-time, load-time work; `packed` must not
- * overlap the sources.  Returns MOE_ERR_WORKSPACE if packed_bytes is smaller
- * than moe_packed_size(cfg). */
+ * lane owns one weight row).  One-time, load-time work, in the role of the
+ * checkpoint loading step of the vLLM recipe page ("Single-GPU int4": a
+ * pack-quantized checkpoint, symmetric W4, group_size 32, routed experts
+ * only).  src: host struct of DEVICE pointers in the moe_weights_plain
+ * layout; packed: device buffer of packed_bytes, owned by the caller, which
+ * must not overlap the sources.  Returns MOE_ERR_NULL for a missing pointer
+ * (the shared pointers must be NULL iff has_shared == 0), MOE_ERR_ALIGN for
+ * a misaligned one, MOE_ERR_WORKSPACE if packed_bytes is smaller than
+ * moe_packed_size(cfg). */
 int moe_pack_weights(const moe_config* cfg /* host */, const moe_weights_plain* src /* host struct */,
                      void* packed, size_t packed_bytes, void* stream);
 
-/* Workspace bytes needed for calls with up to max_tokens tokens. */
+/* Workspace bytes needed for calls with up to max_tokens tokens (the
+ * hand-off words, per-call scratch and the sticky error word of every call
+ * below; the caller allocates it on the device).  0 on an invalid config or
+ * max_tokens < 0. */
 size_t moe_workspace_size(const moe_config* cfg /* host */, int32_t max_tokens);
 
 /* Zero-fill a workspace (a kernel, not hipMemset, so it may be captured).
@@ -107,24 +119,42 @@ int moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
 /* flags for moe_route */
 #define MOE_F_INPUT_RMSNORM 0x1u  /* x is the previous layer's output y: route
                                      rmsnorm(y) = bf16(y / sqrt(mean(y^2) + 1e-6))
-                                     (unit gain) and write it to x_norm [M][H]   */
+                                     (unit gain) and write it to x_norm [M][H].
+                                     x_norm must not overlap x: the call reads x
+                                     while it writes x_norm (MOE_ERR_SHAPE).    */
 
-/* Router GEMV + top-k + softmax weights (steps a1, a2).
- *   router_w [E][H] fp32, x [M][H] bf16 -> topk_ids [M][k] int32 (largest
- *   logit first, ties -> lower id), topk_w [M][k] fp32 (softmax over the
- *   chosen logits; sums to 1).
- * M = 0 is a no-op.  x_norm is required iff MOE_F_INPUT_RMSNORM is set. */
+/* The router: every token goes to top_k of the n_experts routed experts
+ * (bpdata.com Ling-3.0-flash MoE article, "Modell és kiinduló konfiguráció":
+ * eight of 512 per token in every MoE layer; vLLM recipe page, Overview).
+ *   router_w [E][H] fp32 row-major (one row per expert), x [M][H] bf16
+ *   -> topk_ids [M][k] int32 (largest logit first, ties -> lower id),
+ *      topk_w [M][k] fp32 (softmax over the chosen logits; sums to 1).
+ * All arrays are device memory owned by the caller; ws is the caller's
+ * workspace of ws_bytes (moe_workspace_size for at least M tokens).
+ * M = 0 is a no-op.  x_norm is required iff MOE_F_INPUT_RMSNORM is set and
+ * must not overlap x.  Errors: MOE_ERR_NULL, MOE_ERR_ALIGN (16 bytes for
+ * router_w, x, x_norm and ws; 4 for ids and weights), MOE_ERR_SHAPE (M < 0,
+ * unknown flags, x_norm overlapping x), MOE_ERR_WORKSPACE, MOE_ERR_UNSUPPORTED,
+ * MOE_ERR_LAUNCH; nothing is launched on an error. */
 int moe_route(const moe_config* cfg /* host */, const float* router_w, const uint16_t* x,
               int32_t M, uint32_t flags, uint16_t* x_norm, int32_t* topk_ids, float* topk_w,
               void* ws, size_t ws_bytes, void* stream);
 
-/* Expert FFNs + weighted combine (steps a3-a7): for every token, the k
- * routed experts named by topk_ids (used as given: not renormalised;
- * duplicates are summed slot by slot) weighted by topk_w, plus the shared
- * expert with weight 1.  Each distinct expert of the call is read once and
- * applied to all of its tokens.  out [M][H] bf16 (round to nearest even).
- * `packed` is the output of moe_pack_weights for the same cfg.
- * M = 0 is a no-op. */
+/* The expert FFNs and their weighted sum: for every token, the k routed
+ * experts named by topk_ids (used as given: not renormalised; duplicates are
+ * summed slot by slot) weighted by topk_w, plus the one shared expert with
+ * weight 1 (bpdata.com article, "Modell és kiinduló konfiguráció": eight
+ * routed experts and a shared one per token; vLLM recipe page, "Single-GPU
+ * int4": the routed experts symmetric W4 with groups of 32, the shared
+ * expert BF16).  Each distinct expert of the call is read once and applied
+ * to all of its tokens, as a multi-token verify step needs (bpdata.com,
+ * "Optimalizáció 3": a 4-token verify touches up to 32 experts).
+ *   packed: the output of moe_pack_weights for the same cfg; x [M][H] bf16;
+ *   topk_ids [M][k] int32, topk_w [M][k] fp32 -> out [M][H] bf16 (round to
+ *   nearest even).  All device memory owned by the caller; ws as for
+ *   moe_route.  An id outside [0, E) sets bit 0 of the device error word
+ *   and its slot adds nothing.  M = 0 is a no-op.  Errors as for moe_route
+ *   (alignment: 16 bytes for packed, x, out and ws). */
 int moe_forward_w4a16(const moe_config* cfg /* host */, const void* packed, const uint16_t* x,
                       int32_t M, const int32_t* topk_ids, const float* topk_w, uint16_t* out,
                       void* ws, size_t ws_bytes, void* stream);
@@ -133,7 +163,9 @@ int moe_forward_w4a16(const moe_config* cfg /* host */, const void* packed, cons
 #define MOE_F_ONE_LAUNCH 0x2u  /* use the one-launch kernel for every M it supports
                                   (M*top_k <= 64), not only for M = 1 */
 
-/* One whole layer for a step of M tokens: moe_route followed by
+/* One whole MoE layer for a step of M tokens (a Ling-3.0-flash MoE layer's
+ * routed experts and shared expert, as moe_route and moe_forward_w4a16
+ * define them): moe_route followed by
  * moe_forward_w4a16 on the ids and weights it produced (topk_ids, topk_w,
  * x_norm and out are all written; ids, weights and x_norm are those of
  * moe_route bit for bit).  For one token (decode) the router, the top-k and
@@ -142,20 +174,26 @@ int moe_forward_w4a16(const moe_config* cfg /* host */, const void* packed, cons
  * their rounding (the expert h is kept as scaled fp16 instead of a bf16
  * pair).  Otherwise it is the two calls, unless MOE_F_ONE_LAUNCH asks for the
  * one launch.  flags: MOE_F_INPUT_RMSNORM as for moe_route (the experts then
- * see x_norm), MOE_F_ONE_LAUNCH.  Concurrent calls on one workspace race.
- * M = 0 is a no-op. */
+ * see x_norm, which must not overlap x), MOE_F_ONE_LAUNCH.  Concurrent calls
+ * on one workspace race.  The single launch stands in for the pages' CUDA
+ * graphs, which cut the per-kernel launch cost that dominates when few
+ * experts are active (ainews.surl.tw item on Ling-3.0-flash INT4 at 38.7
+ * tok/s, body; ai-radar.it article on the two flags, body).  Errors as for
+ * moe_route and moe_forward_w4a16.  M = 0 is a no-op. */
 int moe_layer_w4a16(const moe_config* cfg /* host */, const float* router_w, const void* packed,
                     const uint16_t* x, int32_t M, uint32_t flags, uint16_t* x_norm,
                     int32_t* topk_ids, float* topk_w, uint16_t* out,
                     void* ws, size_t ws_bytes, void* stream);
 
-/* The two stages of moe_forward_w4a16, for callers that schedule them
+/* The two stages of moe_forward_w4a16 (the gate_up/SiLU half and the
+ * down/combine half of the expert FFNs moe_forward_w4a16 cites), for callers
+ * that schedule them
  * separately (moe_forward_w4a16 = moe_gate_up_w4a16 then moe_down_w4a16 on
  * the same workspace, stream, M and topk_ids).
  * moe_gate_up_w4a16: h = silu(W1 x) * (W3 x) for every (token, slot) and the
- *   shared expert, kept in the workspace (steps a3, a4, a6).
+ *   shared expert, kept in the workspace.
  * moe_down_w4a16: the down projections of those h and the weighted combine
- *   into out [M][H] bf16 (steps a5, a6).  It reads the workspace written by
+ *   into out [M][H] bf16.  It reads the workspace written by
  *   the preceding moe_gate_up_w4a16 of the same M and topk_ids. */
 int moe_gate_up_w4a16(const moe_config* cfg /* host */, const void* packed, const uint16_t* x,
                       int32_t M, const int32_t* topk_ids, void* ws, size_t ws_bytes, void* stream);
@@ -163,7 +201,10 @@ int moe_down_w4a16(const moe_config* cfg /* host */, const void* packed, int32_t
                    const int32_t* topk_ids, const float* topk_w, uint16_t* out,
                    void* ws, size_t ws_bytes, void* stream);
 
-/* Token -> expert grouping of the M*k (token, slot) pairs (step a3):
+/* Token -> expert grouping of the M*k (token, slot) pairs, the step that
+ * lets each expert's weights be read once for all of its tokens in a verify
+ * or prefill batch (bpdata.com article, "Optimalizáció 3"; vLLM recipe page,
+ * chunked prefill):
  * counts [E] int32, offsets [E+1] int32 (exclusive prefix sum), perm [M*k]
  * int32 = flat pair index t*k + j, grouped by expert, ascending inside each
  * expert.  Pairs with an out-of-range id are left out and recorded in the
@@ -179,6 +220,17 @@ int moe_permute(const moe_config* cfg /* host */, const int32_t* topk_ids, int32
 int moe_get_device_error(void* ws, void* stream, int32_t* code_host /* host */);
 
 const char* moe_status_string(int status);
+
+/* Measurement aid, not part of the layer: reads `bytes` of device memory at
+ * `buf` once (16-byte loads, `blocks` workgroups of 256 threads striding over
+ * the buffer) and writes nothing unless the xor of the data equals a fixed
+ * value (then one word per workgroup into sink[blocks], device memory).  The
+ * pages find decode bound by weight reads (bpdata.com article, intro), so the
+ * layer's bandwidth is reported against the rate this plain read reaches on
+ * the same part as well as against the nominal peak.  buf 16-byte aligned,
+ * bytes a multiple of 16 (MOE_ERR_ALIGN), 1 <= blocks <= 65536
+ * (MOE_ERR_SHAPE). */
+int moe_probe_read(const void* buf, size_t bytes, uint32_t* sink /* [blocks] */, int32_t blocks, void* stream);
 
 /* Static description of the compiled library: target arch, kernel variants and the
  * packed-layout tag, for logging next to every measurement. */

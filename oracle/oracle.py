@@ -19,7 +19,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
-LIB_PATH = os.path.join(_HERE, "libmoe_oracle.so")
+# MOE_ORACLE_LIB names another build of moe_oracle.c to load instead (the
+# mutation test loads deliberately broken copies this way, in a child process).
+LIB_PATH = os.environ.get("MOE_ORACLE_LIB") or os.path.join(_HERE, "libmoe_oracle.so")
 _lock = threading.Lock()
 _lib = None
 

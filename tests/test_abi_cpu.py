@@ -115,3 +115,37 @@ def test_pointer_and_size_validation(lib):
     assert lib.moe_workspace_init(odd, 64, None) == -3
     code = ctypes.c_int32(0)
     assert lib.moe_get_device_error(None, None, ctypes.byref(code)) == -1
+
+
+def test_rmsnorm_output_must_not_overlap_input(lib):
+    """With MOE_F_INPUT_RMSNORM the call writes x_norm while other
+    workgroups of the same launch still read x: an overlap is refused before
+    anything is launched (moe_route and moe_layer_w4a16)."""
+    c = _cfg()
+    H = c.hidden
+    base = 0x100000
+    a = ctypes.c_void_p(base)
+    big = 1 << 40
+    rms = B.MOE_F_INPUT_RMSNORM
+    for M in (1, 4):
+        row = H * 2
+        for xn in (base, base + 16, base + M * row - 16):       # in place, shifted inside x
+            p = ctypes.c_void_p(xn)
+            assert lib.moe_route(ctypes.byref(c), a, a, M, rms, p, a, a, a, big, None) == -2, (M, xn)
+            assert lib.moe_layer_w4a16(ctypes.byref(c), a, a, a, M, rms, p, a, a, a, a, big, None) == -2, (M, xn)
+        # adjacent but disjoint buffers pass this check (and then fail the
+        # workspace-size check, so nothing is launched)
+        after = ctypes.c_void_p(base + M * row)
+        assert lib.moe_route(ctypes.byref(c), a, a, M, rms, after, a, a, a, 16, None) == -4
+        before = ctypes.c_void_p(base - M * row)
+        assert lib.moe_layer_w4a16(ctypes.byref(c), a, a, a, M, rms, before, a, a, a, a, 16, None) == -4
+
+
+def test_read_probe_validation(lib):
+    a = ctypes.c_void_p(0x10000)
+    assert lib.moe_probe_read(None, 64, a, 8, None) == -1
+    assert lib.moe_probe_read(a, 64, None, 8, None) == -1
+    assert lib.moe_probe_read(ctypes.c_void_p(0x10004), 64, a, 8, None) == -3
+    assert lib.moe_probe_read(a, 65, a, 8, None) == -3
+    assert lib.moe_probe_read(a, 64, a, 0, None) == -2
+    assert lib.moe_probe_read(a, 0, a, 8, None) == 0

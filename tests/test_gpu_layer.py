@@ -29,9 +29,8 @@ def _gpu():
 
 
 @pytest.fixture(scope="module")
-def ling():
-    _say("generating Ling-shape layer (seed 1)")
-    return DeviceLayer(synth.make_layer(synth.LING, 1), max_tokens=16)
+def ling(ling_seed1):
+    return DeviceLayer(ling_seed1, max_tokens=16)
 
 
 def _layer(dl, x_dev, flags=None, x_norm=None):
@@ -159,9 +158,10 @@ def test_layer_rmsnorm(ling, oracle_mod, M):
     check_out(from_dev_bf16(out), ref, f"layer rmsnorm M={M}")
 
 
-def test_layer_graph_replay(ling):
+def test_layer_graph_replay(ling, oracle_mod):
     """The one-launch layer captured in a graph: every replay (with eager
-    work and synchronisations in between) gives the eager bits."""
+    work and synchronisations in between) gives the eager bits, and meets
+    the oracle."""
     import torch
     from w4a16_grouped_quantized_amd import binding as B
     shape = synth.LING
@@ -188,6 +188,12 @@ def test_layer_graph_replay(ling):
         torch.cuda.synchronize()
         assert torch.equal(got_ids, e_ids) and torch.equal(got_w, e_w), f"replay {t}"
         assert torch.equal(got.view(torch.int16), e_out.view(torch.int16)), f"replay {t}"
+        x1 = xs[t:t + 1]
+        ids_o, _, gap, logits_o = oracle_mod.route(shape, ling.layer.router_w, x1)
+        w_ref = check_ids(shape, got_ids.cpu().numpy(), got_w.cpu().numpy(), ids_o, gap, logits_o)
+        ref, bad = oracle_mod.forward(shape, ling.layer, x1, got_ids.cpu().numpy(), w_ref)
+        assert bad == 0
+        check_out(from_dev_bf16(got), ref, f"graph replay {t}")
     assert ling.device_error() == 0
 
 

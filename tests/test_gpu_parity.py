@@ -35,9 +35,8 @@ def tiny():
 
 
 @pytest.fixture(scope="module")
-def ling_layer():
-    _say("generating Ling-shape layer (seed 1)")
-    return synth.make_layer(synth.LING, 1)
+def ling_layer(ling_seed1):
+    return ling_seed1
 
 
 @pytest.fixture(scope="module")
@@ -106,7 +105,7 @@ def test_ling_determinism(ling):
     x = to_dev_bf16(synth.make_tokens(synth.LING, 3, 4))
     ref_ids, ref_w = ling.route(x)
     ref = ling.forward(x, ref_ids, ref_w)
-    for _ in range(20):
+    for _ in range(100):
         ids, w = ling.route(x)
         out = ling.forward(x, ids, w)
         assert torch.equal(ids, ref_ids) and torch.equal(w, ref_w)
@@ -267,7 +266,7 @@ def test_ling_prefill_chunk_4096_sampled(ling_big, oracle_mod):
 # ------------------------------------------------------------------ stacked layers
 
 @pytest.mark.parametrize("M", [1, 3])
-def test_stack_three_layers_rmsnorm_teacher_forced(ling, oracle_mod, M):
+def test_stack_three_layers_rmsnorm_teacher_forced(ling, ling_seed23, oracle_mod, M):
     """Three independent Ling-shape layers, each fed the previous layer's
     output through the fused unit-gain RMSNorm (eps 1e-6) of the routing
     call.  Every layer is checked against the oracle on the GPU's own
@@ -277,8 +276,7 @@ def test_stack_three_layers_rmsnorm_teacher_forced(ling, oracle_mod, M):
     import torch
     from w4a16_grouped_quantized_amd import binding as B
     shape = synth.LING
-    _say("generating stacked layers (seeds 2, 3)")
-    stack = [ling] + [DeviceLayer(synth.make_layer(shape, s, threads=16), max_tokens=64) for s in (2, 3)]
+    stack = [ling] + [DeviceLayer(layer, max_tokens=64) for layer in ling_seed23]
     x = synth.make_tokens(shape, 60 + M, M)
     y_dev = to_dev_bf16(x)
     for li, dl in enumerate(stack):

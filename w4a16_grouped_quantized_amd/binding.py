@@ -27,7 +27,7 @@ STATUS_NAMES = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_E
 # Every symbol include/moe_w4a16.h declares.
 EXPORTS = ("moe_packed_size", "moe_pack_weights", "moe_workspace_size", "moe_workspace_init",
            "moe_route", "moe_forward_w4a16", "moe_layer_w4a16", "moe_gate_up_w4a16", "moe_down_w4a16", "moe_permute",
-           "moe_get_device_error", "moe_status_string", "moe_build_info")
+           "moe_get_device_error", "moe_status_string", "moe_build_info", "moe_probe_read")
 
 
 class MoeError(RuntimeError):
@@ -81,6 +81,7 @@ def lib() -> ctypes.CDLL:
             L.moe_status_string.argtypes = [ctypes.c_int]
             L.moe_build_info.restype = ctypes.c_char_p
             L.moe_build_info.argtypes = []
+            L.moe_probe_read.argtypes = [_P, ctypes.c_size_t, _P, ctypes.c_int32, _P]
             _lib = L
         return _lib
 
@@ -172,6 +173,11 @@ def permute(cfg, topk_ids, counts, offsets, perm, ws, stream=None):
     _check("moe_permute", lib().moe_permute(ctypes.byref(cfg), _ptr(topk_ids), M, _ptr(counts), _ptr(offsets),
                                             _ptr(perm), _ptr(ws), ws.numel() * ws.element_size(),
                                             _stream(stream)))
+
+
+def probe_read(buf, sink, blocks: int, stream=None):
+    _check("moe_probe_read", lib().moe_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                                  blocks, _stream(stream)))
 
 
 def get_device_error(ws, stream=None) -> int:

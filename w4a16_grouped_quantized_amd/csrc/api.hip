@@ -1,4 +1,4 @@
-// api.cpp — the C ABI (include/moe_w4a16.h): argument checks, workspace and
+// api.hip — the C ABI (include/moe_w4a16.h): argument checks, workspace and
 // packed-layout bookkeeping, and the launches.  Nothing here allocates device
 // memory or synchronises except moe_get_device_error.
 #include "moe_w4a16.h"
@@ -24,6 +24,12 @@ bool experts_gemm(const Shape& s, int M) { return (int64_t)M * s.k >= kPrefillMi
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// True if the byte ranges [a, a + n) and [b, b + n) share a byte.
+bool overlap(const void* a, const void* b, size_t n) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + n && y < x + n;
+}
 
 // Shape checks shared by every entry point.
 int check_cfg(const moe_config* c, Shape* s) {
@@ -97,6 +103,8 @@ int moe_route(const moe_config* cfg, const float* router_w, const uint16_t* x, i
   if (!aligned16(router_w) || !aligned16(x) || !aligned16(ws) || !aligned4(topk_ids) || !aligned4(topk_w) ||
       (rms && !aligned16(x_norm)))
     return MOE_ERR_ALIGN;
+  // the normalised tokens are written while other workgroups still read x
+  if (rms && overlap(x, x_norm, (size_t)M * s.H * 2)) return MOE_ERR_SHAPE;
   if (route_gemm(s, M) && !rms) {
     const PfLayout P = pf_layout(s.H, s.E, s.k, s.I, s.has_shared, M);
     if (ws_bytes < P.total) return MOE_ERR_WORKSPACE;
@@ -198,6 +206,7 @@ int moe_layer_w4a16(const moe_config* cfg, const float* router_w, const void* pa
   if (!aligned16(router_w) || !aligned16(packed) || !aligned16(x) || !aligned16(out) || !aligned16(ws) ||
       !aligned4(topk_ids) || !aligned4(topk_w) || (rms && !aligned16(x_norm)))
     return MOE_ERR_ALIGN;
+  if (rms && overlap(x, x_norm, (size_t)M * s.H * 2)) return MOE_ERR_SHAPE;
   if (one && layer_supported(s, M) && route_supported(s)) {
     WsLayout L;
     rc = check_experts(cfg, &s, packed, x, M, topk_ids, topk_w, out, ws, ws_bytes, true, true, &L);

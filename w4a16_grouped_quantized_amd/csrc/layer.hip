@@ -30,9 +30,16 @@
 // high half holds the call's tag: data and its readiness travel together, so
 // no counter, fence or reset sits between a producer and its readers, and
 // data of earlier calls (or left by other paths) can never pass as this
-// call's.  Waits only ever point at workgroups with smaller ids, which the
-// hardware dispatches first, so every wait ends; each poll is bounded anyway
-// and records bit 1 of the error word if it gives up.  Words crossing
+// call's.  Every wait but one points at workgroups with smaller ids, which
+// the hardware dispatches first.  The exception is the leader (workgroup 0),
+// which waits for every other workgroup's arrival before it advances the
+// epoch; no workgroup waits for the leader after it starts that wait (the
+// RMSNorm flags are set before it).  So the grid makes progress as long as
+// one workgroup slot besides the leader's is free, and workgroups are
+// dispatched in id order; the decode grid (737 workgroups for the Ling
+// shape at one token, at most three per CU by the register budget) is
+// resident at once on the 256 CUs anyway.  Each poll is bounded and records
+// bit 1 of the error word if it gives up.  Words crossing
 // workgroups are stored agent-coherently (written through to memory, past the
 // XCD's L2, which is not coherent with the others); a 64-bit word is stored
 // and loaded whole, so its tag and payload always belong together.

@@ -25,6 +25,7 @@
 //   [2] max over r < I of ||gate row r||_2 * ||up row r||_2 (dequantised),
 //   [3] max over the down rows of ||down row||_1 (dequantised).
 #pragma once
+#include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -42,9 +43,7 @@ struct KSplit {
   int W, GW, P;
 };
 
-#if defined(__HIPCC__)
 __host__ __device__
-#endif
 inline KSplit ksplit_for(int groups) {
   KSplit s;
   s.W = (groups % 4 == 0) ? 4 : (groups % 2 == 0 ? 2 : 1);
@@ -59,9 +58,7 @@ struct SharedSplit {
   int KS, CW;
 };
 
-#if defined(__HIPCC__)
 __host__ __device__
-#endif
 inline SharedSplit shared_split_for(int K, int target_chunks_per_wave) {
   SharedSplit s{1, K / 8 / kWavesPerBlock};
   // largest KS with K/8/4 divisible by KS and chunks per wave >= target
@@ -86,9 +83,7 @@ struct PackedLayout {
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-#if defined(__HIPCC__)
 __host__ __device__
-#endif
 inline PackedLayout packed_layout(int H, int E, int I, int has_shared) {
   PackedLayout L;
   L.gu_q_stride = (size_t)2 * I * H / 2;
@@ -108,9 +103,7 @@ inline PackedLayout packed_layout(int H, int E, int I, int has_shared) {
 }
 
 // Row of matrix tile b served by lane l.
-#if defined(__HIPCC__)
 __host__ __device__
-#endif
 inline int gu_row(int b, int l, int I) { return l < 32 ? 32 * b + l : I + 32 * b + (l - 32); }
 
 }  // namespace moe
