@@ -161,7 +161,7 @@ int moe_forward_w4a16(const moe_config* cfg /* host */, const void* packed, cons
 
 /* flag for moe_layer_w4a16 */
 #define MOE_F_ONE_LAUNCH 0x2u  /* use the one-launch kernel for every M it supports
-                                  (M*top_k <= 64), not only for M = 1 */
+                                  (M <= 4 and M*top_k <= 64), not only for M = 1 */
 
 /* One whole MoE layer for a step of M tokens (a Ling-3.0-flash MoE layer's
  * routed experts and shared expert, as moe_route and moe_forward_w4a16

@@ -64,7 +64,7 @@ def _check_layer(dl, oracle, x_bits, what):
 
 @pytest.mark.parametrize("M", [1, 2, 4, 8, 9])
 def test_layer_ling_matches_oracle(ling, oracle_mod, M):
-    # M <= 8: one launch (M*k <= 64 pairs); M = 9: the two-call path
+    # M <= 4: one launch; M = 8, 9: the two-call path
     steps = 24 if M == 1 else 4
     x = synth.make_tokens(synth.LING, 500 + M, steps * M)
     worst = max(_check_layer(ling, oracle_mod, x[s * M:(s + 1) * M], f"layer ling M={M} step {s}") for s in range(steps))
@@ -75,9 +75,9 @@ def test_layer_after_larger_calls(ling, oracle_mod):
     """Calls of different M share one workspace: the per-call arrays of a
     large call overlap where a small call's arrays live, so the one-launch
     path must keep its flags and counters in the fixed header.  A 9-token
-    call (two-call path, fills the arrays with data) and an 8-token one-launch
+    call (two-call path, fills the arrays with data) and a 4-token one-launch
     call, then single tokens, each checked against the oracle."""
-    for M in (9, 8, 1, 9, 1):
+    for M in (9, 4, 1, 9, 1):
         x = synth.make_tokens(synth.LING, 900 + M, M)
         _check_layer(ling, oracle_mod, x, f"layer after larger calls, M={M}")
 

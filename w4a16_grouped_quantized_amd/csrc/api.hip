@@ -212,8 +212,11 @@ int moe_layer_w4a16(const moe_config* cfg, const float* router_w, const void* pa
     rc = check_experts(cfg, &s, packed, x, M, topk_ids, topk_w, out, ws, ws_bytes, true, true, &L);
     if (rc != MOE_OK) return rc;
     const PackedLayout P = packed_layout(s.H, s.E, s.I, s.has_shared);
-    return launched(launch_layer(s, static_cast<const uint8_t*>(packed), P, router_w, x, M, true, rms, kRmsEps, x_norm,
-                                 topk_ids, topk_w, out, static_cast<uint8_t*>(ws), L, static_cast<hipStream_t>(stream)));
+    const hipError_t e = launch_layer(s, static_cast<const uint8_t*>(packed), P, router_w, x, M, true, rms, kRmsEps,
+                                      x_norm, topk_ids, topk_w, out, static_cast<uint8_t*>(ws), L,
+                                      static_cast<hipStream_t>(stream));
+    // a device that cannot hold the whole grid at once takes the two calls
+    if (e != hipErrorInvalidConfiguration) return launched(e);
   }
   rc = moe_route(cfg, router_w, x, M, flags & MOE_F_INPUT_RMSNORM, x_norm, topk_ids, topk_w, ws, ws_bytes, stream);
   if (rc != MOE_OK) return rc;

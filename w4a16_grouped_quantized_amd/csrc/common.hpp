@@ -37,19 +37,22 @@ constexpr int kRouteCounters = 1 + (512 / 4 + kArriveFan - 1) / kArriveFan;
 
 // Workgroup roles of the one-launch small-M layer, in launch order: the
 // leader (workgroup 0: the call's tag, the normalised tokens), router rows
-// (4 per workgroup, only when the launch routes), shared gate_up (tile x K
+// (4 per workgroup) and selectors (the top-k, published in kSelectors
+// copies), both only when the launch routes, shared gate_up (tile x K
 // slice), routed gate_up (slot x gate_up tile; slots past the number of
 // distinct experts have nothing to do), down (kDnRows output rows each:
 // every routed and the shared down projection of those rows, and the
 // output).  S = M*k (token, slot) pairs bound the distinct-expert units.
 struct LayerGrid {
-  int gSG, gGU, gDN, grid;  // the router rows are workgroups 1 .. gSG-1
+  int gSL, gSG, gGU, gDN, grid;  // router rows: workgroups 1 .. gSL-1; selectors gSL .. gSG-1
 };
 constexpr int kDnRows = 8;
+constexpr int kSelectors = 8;
 inline LayerGrid layer_roles(int H, int E, int I, int has_shared, int route, int M, int k) {
   const SharedSplit sg = shared_gu_split(H);
   LayerGrid g;
-  g.gSG = 1 + (route ? (E + 3) / 4 : 0);
+  g.gSL = 1 + (route ? (E + 3) / 4 : 0);
+  g.gSG = g.gSL + (route ? kSelectors : 0);
   g.gGU = g.gSG + (has_shared ? (I / 32) * sg.KS : 0);
   g.gDN = g.gGU + M * k * (I / 32);
   g.grid = g.gDN + H / kDnRows;
@@ -70,8 +73,8 @@ struct WsHeader {
   size_t dn_cnt;     // int32 [H/64] spaced: partial rows finished per down tile
   size_t epoch;      // uint32: tag of the last one-launch call
   size_t arrive;     // int32 [kArriveCounters] spaced: workgroups that have read the epoch this call
-  size_t flags;      // uint64 [largest one-launch grid]: normalised tokens ready, per workgroup (cleared by it)
   size_t rkeys;      // uint64 [kMaxLayerKeys]: router logits [M][E] as order-preserving keys | tag
+  size_t rrec;       // uint64 [kSelectors][2][kMaxUnits]: the routing (ids | tag, weight bits | tag) per selector
   size_t hval;       // uint64 [kMaxUnits][I/32][16]: h per (slot, tile) as fp16 pairs | tag
   size_t hmeta;      // uint64 [kMaxUnits][I/32]: the power-of-two exponent of that h | tag
   size_t hsh;        // uint64 [kMaxUnits][I]: shared-expert h per token, fp32 bits | tag
@@ -90,9 +93,8 @@ inline size_t ws_header(int H, int E, int I, int has_shared, WsHeader* w) {
   w->dn_cnt = take(cs * (H / 64));
   w->epoch = take(4);
   w->arrive = take(cs * kArriveCounters);
-  // the largest grid: M*k and M both at kMaxUnits (k = 1)
-  w->flags = take((size_t)8 * layer_roles(H, E, I, has_shared, 1, kMaxUnits, 1).grid);
   w->rkeys = take((size_t)kMaxLayerKeys * 8);
+  w->rrec = take((size_t)kSelectors * 2 * kMaxUnits * 8);
   w->hval = take((size_t)kMaxUnits * (I / 32) * 16 * 8);
   w->hmeta = take((size_t)kMaxUnits * (I / 32) * 8);
   w->hsh = take(has_shared ? (size_t)kMaxUnits * I * 8 : 0);
@@ -383,31 +385,8 @@ __device__ __forceinline__ void store_hilo_coherent(uint16_t* __restrict__ group
   st_coherent(&group_base[32 + i], lo);
 }
 
-// Hand-off flag inside one launch: thread 0 polls *f (agent-coherent) until it
-// is non-zero, then clears it for the next call (the flag belongs to this
-// workgroup alone); the workgroup then follows a full barrier (its acquire
-// fence keeps every later load of the workgroup after the poll).  Loads
-// after it that read the producer's data must be agent-coherent.  The
-// producer sets the flag only after its data stores have completed.  A wait
-// that gives up after kSpinLimit polls sets bit 1 of the error word.
+// Polls that give up after this many rounds set bit 1 of the error word.
 constexpr int kSpinLimit = 1 << 22;
-__device__ __forceinline__ uint64_t wait_flag(uint64_t* f, int32_t* err, uint64_t* lds_val) {
-  if (threadIdx.x == 0) {
-    int spins = 0;
-    uint64_t v;
-    while ((v = ld_coherent(f)) == 0) {
-      if (++spins > kSpinLimit) {
-        atomicOr(err, 2);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
-    st_coherent(f, (uint64_t)0);
-    *lds_val = v;
-  }
-  __syncthreads();
-  return *lds_val;
-}
 
 // A pointer passed through an empty asm after a wait: loads through it
 // (scalar loads from the constant address space in particular, which the

@@ -249,6 +249,55 @@ __device__ __forceinline__ float routed_dot(const uint4 (&wq)[GW], const ScalePa
   return acc;
 }
 
+// routed_dot against an activation staged in LDS (xl: the token's inputs as
+// bf16 pairs in natural order, 16 dwords per group; bias: its group
+// corrections).  Every lane of a wavefront reads the same addresses, so the
+// reads are broadcasts.
+template <int GW, int P>
+__device__ __forceinline__ float routed_dot_lds(const uint4 (&wq)[GW], const ScalePack<P> (&sc)[GW / P],
+                                                const uint32_t* xl, const float* bias, int g0, uint32_t magic) {
+  float acc = 0.f;
+#pragma unroll
+  for (int gi = 0; gi < GW; ++gi) {
+    const uint4* xp = reinterpret_cast<const uint4*>(xl + (g0 + gi) * 16);
+    uint32_t xs[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = xp[q];
+      xs[4 * q] = v.x; xs[4 * q + 1] = v.y; xs[4 * q + 2] = v.z; xs[4 * q + 3] = v.w;
+    }
+    // opaque copies, as in routed_dot: the code-pair extraction and the
+    // scale's conversion stay next to their use instead of being hoisted
+    // out of the caller's token loop (which would hold 16 pairs and a float
+    // per group in registers)
+    uint4 w = wq[gi];
+    asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+    uint32_t sw = sc[gi / P].w[(gi % P) >> 1];
+    asm volatile("" : "+v"(sw));
+    const float scale = ((gi % P) & 1) ? __uint_as_float(sw & 0xFFFF0000u) : __uint_as_float(sw << 16);
+    const float pr = dot_group_q4(w, xs, bias[g0 + gi], magic);
+    acc = fmaf(scale, pr, acc);
+    // one group's activation reads in flight at a time: hoisting them all
+    // would take 16 registers per group
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return acc;
+}
+
+// Shared BF16 rows (CW chunks of 8 inputs from chunk c0 on) against an
+// activation staged in LDS as bf16 pairs (4 dwords per chunk).
+template <int CW>
+__device__ __forceinline__ float shared_dot_lds(const uint4 (&wc)[CW], const uint32_t* xl, int c0) {
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < CW; ++c) {
+    const uint4 v = *reinterpret_cast<const uint4*>(xl + (c0 + c) * 4);
+    const uint32_t xs[4] = {v.x, v.y, v.z, v.w};
+    acc = dot_chunk_bf16(wc[c], xs, acc);
+  }
+  return acc;
+}
+
 // Shared BF16 rows: CW chunks of 8 inputs from chunk c0 on.
 template <int CW, bool HILO>
 __device__ __forceinline__ float shared_dot(const uint4 (&wc)[CW], const uint16_t* __restrict__ act, int c0) {

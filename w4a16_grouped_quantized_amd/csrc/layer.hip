@@ -6,49 +6,83 @@
 // workgroup role of one grid, in this order:
 //
 //   leader          (workgroup 0) the call's tag: one more than the last
-//                   call's, kept in the workspace; with RMSNorm first the
-//                   normalised tokens; then the tag into every other
-//                   workgroup's flag;
+//                   call's, kept in the workspace; with RMSNorm also the
+//                   normalised tokens for the caller;
 //   router rows     (only when the launch routes) 4 rows each, stored as
 //                   order-preserving keys with the tag;
+//   selectors       (kSelectors, only when the launch routes) each gathers
+//                   every key, runs the top-k and softmax once per token and
+//                   publishes the ids and weights of every slot, tagged, in
+//                   its own copy of the routing record (the first one also
+//                   hands them to the caller);
 //   shared gate_up  tile x K slice of the shared expert; the last slice of a
 //                   tile sums the slices into h_sh (fp32, with the tag);
-//   routed gate_up  (slot u, gate_up tile b): the top-k of every token from
-//                   the keys (or the caller's ids), the distinct experts in
-//                   order of first occurrence ("units"); workgroups u below
-//                   their number take unit u's expert and compute h of the
-//                   tile's 32 rows for every token routed to it, stored as
-//                   fp16 pairs under a power-of-two scale, with the tag;
-//   down            (16 output rows): the same routing, the down rows of
-//                   every slot's expert requested at once and the shared
-//                   expert's rows at the start, then waits for the h of the
-//                   token's slots and the shared h, and writes
-//                   out = sum_slots w * (W_down h) + W_shared_down h_sh.
+//   routed gate_up  (unit u, gate_up tile b): reads a routing record, finds
+//                   the distinct experts in order of first occurrence
+//                   ("units"); workgroups u below their number take unit
+//                   u's expert and compute h of the tile's 32 rows for every
+//                   token routed to it, stored as fp16 pairs under a
+//                   power-of-two scale, with the tag;
+//   down            (8 output rows): reads a routing record, requests the
+//                   down rows of every slot's expert (the shared expert's at
+//                   the start), then polls the shared h and the h records and
+//                   writes out = sum_slots w * (W_down h) + W_shared_down h_sh.
 //
-// Every workgroup reads the tag from its flag (set only by the leader,
-// cleared by its owner).  A consumer polls the words it needs until their
-// high half holds the call's tag: data and its readiness travel together, so
-// no counter, fence or reset sits between a producer and its readers, and
-// data of earlier calls (or left by other paths) can never pass as this
-// call's.  Every wait but one points at workgroups with smaller ids, which
-// the hardware dispatches first.  The exception is the leader (workgroup 0),
-// which waits for every other workgroup's arrival before it advances the
-// epoch; no workgroup waits for the leader after it starts that wait (the
-// RMSNorm flags are set before it).  So the grid makes progress as long as
-// one workgroup slot besides the leader's is free, and workgroups are
-// dispatched in id order; the decode grid (737 workgroups for the Ling
-// shape at one token, at most three per CU by the register budget) is
-// resident at once on the 256 CUs anyway.  Each poll is bounded and records
-// bit 1 of the error word if it gives up.  Words crossing
-// workgroups are stored agent-coherently (written through to memory, past the
-// XCD's L2, which is not coherent with the others); a 64-bit word is stored
-// and loaded whole, so its tag and payload always belong together.
+// Every workgroup reads the call's tag from the epoch word.  A consumer polls
+// the words it needs until their high half holds the call's tag: data and its
+// readiness travel together, so no counter, fence or reset sits between a
+// producer and its readers, and data of earlier calls (or left by other
+// paths) can never pass as this call's.  Every wait but one points at
+// workgroups with smaller ids, which the hardware dispatches first.  The
+// exception is the leader (workgroup 0), which waits for every other
+// workgroup's arrival before it advances the epoch; no workgroup waits for
+// the leader.  So the grid makes progress as long as one workgroup slot
+// besides the leader's is free and workgroups are dispatched in id order;
+// the host also refuses the launch unless the device can hold the whole grid
+// at once.  Each poll is bounded and records bit 1 of the error word if it
+// gives up.  Words crossing workgroups are stored agent-coherently (written
+// through past the XCD's L2, which is not coherent with the others) and
+// polled with agent-coherent loads; a 64-bit word is stored and loaded whole,
+// so its tag and payload always belong together.  Vector loads return in
+// issue order, and a CU serves its wavefronts' requests roughly in order
+// too, so a poll issued behind bulk weight loads on the same CU waits for
+// them; and a product waits for every load issued before its operands, so
+// each role requests its scales before its codes.
 #include <algorithm>
 
 #include "experts_dev.hpp"
 #include "route_dev.hpp"
 
 namespace moe {
+
+// Optional timeline of the launch (a build with -DMOE_LAYER_TRACE only):
+// thread 0 of each workgroup records the realtime clock (10 ns ticks) at
+// numbered points of its role; moe_layer_trace_read copies the records out.
+#ifdef MOE_LAYER_TRACE
+constexpr int kTraceWgs = 2048, kTracePoints = 16;
+__device__ uint64_t g_layer_trace[kTraceWgs * kTracePoints];
+#define LTRACE_AT(p, who)                                                                         \
+  do {                                                                                            \
+    if ((who) && blockIdx.x < kTraceWgs)                                                          \
+      g_layer_trace[blockIdx.x * kTracePoints + (p)] = __builtin_amdgcn_s_memrealtime();          \
+  } while (0)
+#define LTRACE(p) LTRACE_AT(p, threadIdx.x == 0)
+#define LTRACE_WAIT() __builtin_amdgcn_s_waitcnt(0)
+#define LTRACE_ID()                                                                               \
+  do {                                                                                            \
+    if (threadIdx.x == 0 && blockIdx.x < kTraceWgs) {                                             \
+      uint32_t hw, xcc;                                                                           \
+      asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));                            \
+      asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));                          \
+      g_layer_trace[blockIdx.x * kTracePoints + kTracePoints - 1] = ((uint64_t)xcc << 32) | hw;   \
+    }                                                                                             \
+  } while (0)
+#else
+#define LTRACE_AT(p, who) do {} while (0)
+#define LTRACE(p) do {} while (0)
+#define LTRACE_ID() do {} while (0)
+#define LTRACE_WAIT() do {} while (0)
+#endif
 
 struct LayerArgs {
   ExpArgs a;
@@ -58,8 +92,8 @@ struct LayerArgs {
   LayerGrid g;
   uint32_t* __restrict__ epoch;  // tag of the last call
   int32_t* __restrict__ arrive;  // [kArriveCounters] spaced: workgroups that have read the epoch
-  uint64_t* __restrict__ flags;  // [grid] normalised tokens ready (RMSNorm only)
   uint64_t* __restrict__ rkeys;  // [M][E] router keys | tag
+  uint64_t* __restrict__ rrec;   // [kSelectors][2][kMaxUnits] routing records: ids | tag, weight bits | tag
   uint64_t* __restrict__ hval;   // [S][I/32][16] fp16 pairs of h | tag
   uint64_t* __restrict__ hmeta;  // [S][I/32] exponent of the tile's scale | tag
   uint64_t* __restrict__ hsh;    // [M][I] shared h, fp32 bits | tag
@@ -72,7 +106,7 @@ __device__ __forceinline__ uint32_t next_tag(uint32_t epoch) { return epoch + 1u
 
 // The leader: see the file comment.
 template <int NI>
-__device__ void leader(const LayerArgs& A) {
+__device__ __forceinline__ void leader(const LayerArgs& A) {
   const ExpArgs& a = A.a;
   const LayerGrid& G = A.g;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -82,15 +116,9 @@ __device__ void leader(const LayerArgs& A) {
       uint2 packed[NI];
       load_token<NI>(a.x + (size_t)t * a.H, a.H, lane, true, A.r.eps, xv, packed);
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const size_t o = (size_t)t * a.H + 256 * i + 4 * lane;
-        st_coherent(reinterpret_cast<uint64_t*>(A.r.x_norm + o), ((uint64_t)packed[i].y << 32) | packed[i].x);
-      }
+      for (int i = 0; i < NI; ++i)
+        *reinterpret_cast<uint2*>(A.r.x_norm + (size_t)t * a.H + 256 * i + 4 * lane) = packed[i];
     }
-    // the normalised tokens complete before the flags of their readers
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int i = G.gSG + tid; i < G.gDN; i += kBlock) st_coherent(&A.flags[i], (uint64_t)1);
   }
   // the epoch advances once every other workgroup has read it
   if (tid == 0) {
@@ -114,22 +142,22 @@ __device__ void leader(const LayerArgs& A) {
     for (int c = 0; c < kArriveCounters; ++c) st_coherent(&A.arrive[c * kCntStride], 0);
     st_coherent(reinterpret_cast<int32_t*>(A.epoch), (int32_t)T);
   }
+  LTRACE(1);
 }
 
 // The call's tag in a workgroup other than the leader, from the epoch that
 // thread 0 read at the start (ev), and that workgroup's arrival: issued once
-// the epoch load (and the value `after`, if any) has returned.  The leader
-// advances the epoch only after every arrival, so all workgroups of a call
-// read the same epoch.
+// the epoch load has returned.  The leader advances the epoch only after
+// every arrival, so all workgroups of a call read the same epoch.
 __device__ __forceinline__ uint32_t share_tag(uint32_t ev, uint32_t* lds) {
   if (threadIdx.x == 0) *lds = next_tag(ev);
   lds_sync();
   return *lds;
 }
-__device__ __forceinline__ void arrive_epoch(const LayerArgs& A, uint32_t ev, int after = 0) {
+__device__ __forceinline__ void arrive_epoch(const LayerArgs& A, uint32_t ev) {
   if (threadIdx.x == 0) {
     int one = 1;
-    asm volatile("" : "+v"(one) : "v"(ev), "v"(after));
+    asm volatile("" : "+v"(one) : "v"(ev));
     __hip_atomic_fetch_add(&A.arrive[(blockIdx.x % kArriveCounters) * kCntStride], one, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -146,8 +174,7 @@ __device__ __forceinline__ uint32_t read_epoch(const LayerArgs& A) {
 // polls its entries (tid + m * kBlock) agent-coherently until they carry the
 // tag; the workgroup follows.
 constexpr int kKeyBatch = 8;  // key polls issued before their tags are checked
-constexpr uint64_t kDnLoadDelay = 160;  // 1.6 us in s_memrealtime ticks (100 MHz)
-__device__ void gather_keys(const LayerArgs& A, uint32_t T, uint32_t* lkeys) {
+__device__ __forceinline__ void gather_keys(const LayerArgs& A, uint32_t T, uint32_t* lkeys) {
   const int tid = threadIdx.x;
   const int nk = A.a.M * A.a.E;  // <= 32 per thread
   uint32_t todo = 0;
@@ -172,55 +199,114 @@ __device__ void gather_keys(const LayerArgs& A, uint32_t T, uint32_t* lkeys) {
       if (tid == 0) atomicOr(A.a.err, 2);
       break;
     }
-    __builtin_amdgcn_s_sleep(4);
+    __builtin_amdgcn_s_sleep(1);
   }
 }
 
-// ids and weights of every slot into lids / lw (LDS): the top-k of the keys
-// in lkeys (one wavefront per token), or the caller's.
-__device__ void select_slots(const LayerArgs& A, const uint32_t* lkeys, int* topk_lds, int* lids, float* lw,
-                             bool want_w = true) {
+// ids and weights of every slot of every token into lids / lw (LDS): the
+// top-k of the keys in lkeys, one wavefront per token.
+__device__ __forceinline__ void select_slots(const LayerArgs& A, const uint32_t* lkeys, int* topk_lds, int* lids,
+                                             float* lw) {
   const ExpArgs& a = A.a;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (A.route) {
-    for (int t = wave; t < a.M; t += kWavesPerBlock) {
-      uint32_t key[kTopkEPL];
-      bool present[kTopkEPL];
+  for (int t = wave; t < a.M; t += kWavesPerBlock) {
+    uint32_t key[kTopkEPL];
+    bool present[kTopkEPL];
 #pragma unroll
-      for (int j = 0; j < kTopkEPL; ++j) {
-        const int e = lane + kWave * j;
-        present[j] = e < a.E;
-        key[j] = present[j] ? lkeys[t * a.E + e] : 0u;
-      }
-      int id;
-      float w;
-      topk_select(key, present, a.k, lane, topk_lds + wave * 3 * kMaxTopK, id, w, want_w);
-      if (lane < a.k) {
-        lids[t * a.k + lane] = id;
-        lw[t * a.k + lane] = w;
-      }
+    for (int j = 0; j < kTopkEPL; ++j) {
+      const int e = lane + kWave * j;
+      present[j] = e < a.E;
+      key[j] = present[j] ? lkeys[t * a.E + e] : 0u;
     }
-  } else {
-    for (int p = tid; p < a.S; p += kBlock) {
-      lids[p] = a.ids[p];
-      lw[p] = a.topk_w[p];
+    int id;
+    float w;
+    topk_select(key, present, a.k, lane, topk_lds + wave * kTopkLdsInts, id, w, true);
+    if (lane < a.k) {
+      lids[t * a.k + lane] = id;
+      lw[t * a.k + lane] = w;
     }
   }
   lds_sync();
 }
 
+// The ids (and with want_w the weights) of every slot into lids / lw (LDS),
+// by one wavefront: polled from routing record copy c until every word
+// carries the call's tag, or the caller's when the launch does not route.
+__device__ __forceinline__ void routing_wave(const LayerArgs& A, uint32_t T, int c, int lane, int* lids, float* lw,
+                                             bool want_w) {
+  const ExpArgs& a = A.a;
+  if (!A.route) {
+    for (int p = lane; p < a.S; p += kWave) {
+      lids[p] = a.ids[p];
+      if (want_w) lw[p] = a.topk_w[p];
+    }
+    return;
+  }
+  const uint64_t* rec = A.rrec + (size_t)c * 2 * kMaxUnits;
+  bool need = lane < a.S;  // S <= 64: one slot per lane
+  for (int spins = 0;; ++spins) {
+    if (need) {
+      const uint64_t vi = ld_coherent(&rec[lane]);
+      const uint64_t vw = want_w ? ld_coherent(&rec[kMaxUnits + lane]) : tagged(0u, T);
+      if (has_tag(vi, T) && has_tag(vw, T)) {
+        lids[lane] = (int)(uint32_t)vi;
+        if (want_w) lw[lane] = __uint_as_float((uint32_t)vw);
+        need = false;
+      }
+    }
+    if (!__ballot(need)) break;
+    if (spins >= kSpinLimit) {
+      if (lane == 0) atomicOr(a.err, 2);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
 __device__ __forceinline__ bool id_ok(int e, int E) { return e >= 0 && e < E; }
 
-// Three workgroups per CU (at most 168 VGPRs): a decode grid (under 768
-// workgroups) is resident at once, so no role waits for a slot.
+// Tokens a launch takes (all of them are staged in LDS by the workgroups
+// that read them).
+constexpr int kLayerMaxTokens = 4;
+
+// Tokens t0 .. t0+nt-1 into LDS: xl[t * H/2 + d] holds inputs 2d, 2d+1 of
+// token t0+t as bf16 (RMS-normalised when the launch asks, by the same
+// function and in the same order as every other wavefront that normalises,
+// so every copy has the same bits), then gb[t * H/32 + g] the group
+// corrections of each.  Whole-workgroup call.
+template <int NI>
+__device__ __forceinline__ void stage_tokens(const LayerArgs& A, int t0, int nt, uint32_t* xl, float* gb) {
+  const ExpArgs& a = A.a;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int HD = a.H / 2;
+  if (A.rmsnorm) {
+    for (int t = wave; t < nt; t += kWavesPerBlock) {
+      float xv[NI][4];
+      uint2 packed[NI];
+      load_token<NI>(a.x + (size_t)(t0 + t) * a.H, a.H, lane, true, A.r.eps, xv, packed);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) *reinterpret_cast<uint2*>(xl + (size_t)t * HD + 128 * i + 2 * lane) = packed[i];
+    }
+  } else {
+    const int nc = nt * (a.H / 8);  // 16-byte chunks
+    for (int c = tid; c < nc; c += kBlock)
+      reinterpret_cast<uint4*>(xl)[c] = reinterpret_cast<const uint4*>(a.x + (size_t)t0 * a.H)[c];
+  }
+  lds_sync();
+  const int GK = a.H / kGroup;
+  for (int j = tid; j < nt * GK; j += kBlock) gb[j] = group_bias_lds<false>(xl + (size_t)(j / GK) * HD, j % GK);
+  lds_sync();
+}
+
+// Three workgroups per CU (at most 168 VGPRs, LDS within a third of the CU):
+// a decode grid fits on the device at once.
 template <int NI, int GWG, int PG, int CWG, int PD, int NPQ, int NSC, int DG>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void k_layer(const LayerArgs A) {
-  extern __shared__ __align__(16) uint32_t dyn[];  // router keys [M][E], then group corrections [M][H/32]
+  extern __shared__ __align__(16) uint32_t dyn[];  // router keys [M][E], then the staged tokens
   __shared__ float red[kWavesPerBlock][kWave];
   __shared__ int flag;
-  __shared__ uint64_t fval;
   __shared__ uint32_t tag_lds;
-  __shared__ __align__(16) int topk_lds[kWavesPerBlock * 3 * kMaxTopK];
+  __shared__ __align__(16) int topk_lds[kWavesPerBlock * kTopkLdsInts];
   __shared__ int lids[kMaxUnits];
   __shared__ float lw[kMaxUnits];
   __shared__ int uexp[kMaxUnits + 1];      // expert of each unit; [kMaxUnits] = number of units
@@ -236,6 +322,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   const LayerGrid& G = A.g;
   const int tid = threadIdx.x, wave = uniform(tid >> 6), lane = tid & 63;
   const int blk = blockIdx.x;
+  LTRACE(0);
+  LTRACE_ID();
 
   // ------------------------------------------------------------ leader
   if (blk == 0) {
@@ -244,7 +332,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   }
 
   // ------------------------------------------------------------ router rows
-  if (blk < G.gSG) {
+  if (blk < G.gSL) {
     const uint32_t ev = read_epoch(A);
     const int e = (blk - 1) * kWavesPerBlock + wave;
     const bool has_row = e < a.E;
@@ -271,7 +359,37 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const uint32_t T = share_tag(ev, &tag_lds);
     for (int t = lane; t < a.M; t += kWave)
       if (has_row) st_coherent(&A.rkeys[(size_t)t * a.E + e], tagged(sort_key(red[wave][t]), T));
+    LTRACE_WAIT();
+    LTRACE(1);
     arrive_epoch(A, ev);
+    return;
+  }
+
+  // LDS: router keys [M][E] (routing in the launch), then the staged tokens
+  // and their group corrections
+  uint32_t* lkeys = dyn;
+  uint32_t* xl = dyn + (A.route ? a.M * a.E : 0);
+  float* gbias = reinterpret_cast<float*>(xl + (size_t)a.M * (a.H / 2));
+
+  // ------------------------------------------------------------ selectors
+  if (blk < G.gSG) {
+    const uint32_t ev = read_epoch(A);
+    const uint32_t T = take_tag(A, ev, &tag_lds);
+    const int c = blk - G.gSL;
+    gather_keys(A, T, lkeys);
+    LTRACE(1);
+    select_slots(A, lkeys, topk_lds, lids, lw);
+    uint64_t* rec = A.rrec + (size_t)c * 2 * kMaxUnits;
+    for (int p = tid; p < a.S; p += kBlock) {
+      st_coherent(&rec[p], tagged((uint32_t)lids[p], T));
+      st_coherent(&rec[kMaxUnits + p], tagged(__float_as_uint(lw[p]), T));
+      if (c == 0) {  // the routing, for the caller
+        A.r.ids[p] = lids[p];
+        A.r.w[p] = lw[p];
+      }
+    }
+    LTRACE_WAIT();
+    LTRACE(2);
     return;
   }
 
@@ -289,13 +407,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       const uint8_t* base = reinterpret_cast<const uint8_t*>(a.sh_gu) + ((size_t)(b * (a.H / 8) + c0) * kWave + lane) * 16;
 #pragma unroll
       for (int c = 0; c < CWG; ++c) wc[c] = *reinterpret_cast<const uint4*>(base + (size_t)c * kWave * 16);
-      const uint16_t* act = a.x;
-      if (A.rmsnorm) {  // the normalised tokens are ready with the flag
-        wait_flag(&A.flags[blk], a.err, &fval);
-        act = after_wait(static_cast<const uint16_t*>(A.r.x_norm));
-      }
+      stage_tokens<NI>(A, 0, a.M, xl, gbias);
       for (int t = 0; t < a.M; ++t) {
-        red[wave][lane] = shared_dot<CWG, false>(wc, act + (size_t)t * a.H, c0);
+        red[wave][lane] = shared_dot_lds<CWG>(wc, xl + (size_t)t * (a.H / 2), c0);
         lds_sync();
         if (tid < kWave) {
           float part = 0.f;
@@ -319,93 +433,77 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         if (lane < 32)
           st_coherent(&A.hsh[(size_t)t * a.I + 32 * b + lane], tagged(__float_as_uint(silu_f32(part) * up), T));
       }
+      LTRACE_WAIT();
+      LTRACE(2);
       return;
     }
   }
 
-  uint32_t* lkeys = dyn;
-  float* gbias = reinterpret_cast<float*>(dyn) + (A.route ? a.M * a.E : 0);
-
   // ------------------------------------------------------------ routed gate_up
-  // (slot u, gate_up tile b): h of the tile's 32 rows for every token routed
+  // (unit u, gate_up tile b): h of the tile's 32 rows for every token routed
   // to unit u's expert.
   if (blk < G.gDN) {
     const uint32_t ev = read_epoch(A);
     const int idx = blk - G.gGU, u = idx / a.Tgu, b = idx % a.Tgu;
     const int GK = a.H / kGroup;
-    // group corrections of the tokens (the caller's now; normalised ones
-    // once the flag says they are stored)
-    if (!A.rmsnorm)
-      for (int j = tid; j < a.M * GK; j += kBlock) {
-        GroupBias<false> gl;
-        gl.load(a.x + (size_t)(j / GK) * a.H, j % GK);
-        gbias[j] = gl.value();
-      }
-    if (A.rmsnorm) wait_flag(&A.flags[blk], a.err, &fval);
+    stage_tokens<NI>(A, 0, a.M, xl, gbias);
     const uint32_t T = take_tag(A, ev, &tag_lds);
-    const uint16_t* act = A.rmsnorm ? after_wait(static_cast<const uint16_t*>(A.r.x_norm)) : a.x;
-    if (A.rmsnorm)
-      for (int j = tid; j < a.M * GK; j += kBlock) {
-        GroupBias<false> gl;
-        gl.load(act + (size_t)(j / GK) * a.H, j % GK);
-        gbias[j] = gl.value();
-      }
-    if (A.route) gather_keys(A, T, lkeys);
-    // the routed workgroups need the ids only, but the first one also hands
-    // the weights to the caller
-    select_slots(A, lkeys, topk_lds, lids, lw, idx == 0);
+    LTRACE(1);
     // units: distinct valid experts in order of first occurrence (S <= 64);
     // the experts of one routed token are distinct: unit u is slot u
-    if (wave == 0 && A.route && a.M == 1) {
-      if (lane < a.S) {
-        uexp[lane] = lids[lane];
-        umask[lane] = 1ull << lane;
+    if (wave == 0) {
+      routing_wave(A, T, idx % kSelectors, lane, lids, lw, false);
+      if (A.route && a.M == 1) {
+        if (lane < a.S) {
+          uexp[lane] = lids[lane];
+          umask[lane] = 1ull << lane;
+        }
+        if (lane == 0) uexp[kMaxUnits] = a.S;
+      } else {
+        const int id = lane < a.S ? lids[lane] : -1;
+        const bool valid = id_ok(id, a.E);
+        bool first = valid;
+        uint64_t mem = 0;
+        for (int q = 0; q < a.S; ++q) {
+          const int v = __builtin_amdgcn_readlane(id, q);
+          first = first && !(q < lane && v == id);
+          mem |= (uint64_t)(valid && v == id) << q;
+        }
+        const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        const uint64_t fb = __ballot(first);
+        if (first) {
+          const int r = __popcll(fb & lt);
+          uexp[r] = id;
+          umask[r] = mem;
+        }
+        if (lane == 0) uexp[kMaxUnits] = __popcll(fb);
       }
-      if (lane == 0) uexp[kMaxUnits] = a.S;
-    } else if (wave == 0) {
-      const int id = lane < a.S ? lids[lane] : -1;
-      const bool valid = id_ok(id, a.E);
-      bool first = valid;
-      uint64_t mem = 0;
-      for (int q = 0; q < a.S; ++q) {
-        const int v = __builtin_amdgcn_readlane(id, q);
-        first = first && !(q < lane && v == id);
-        mem |= (uint64_t)(valid && v == id) << q;
-      }
-      const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-      const uint64_t fb = __ballot(first);
-      if (first) {
-        const int r = __popcll(fb & lt);
-        uexp[r] = id;
-        umask[r] = mem;
-      }
-      if (lane == 0) uexp[kMaxUnits] = __popcll(fb);
     }
     lds_sync();
-    if (A.route && u == 0 && b == 0)  // the routing, for the caller
-      for (int p = tid; p < a.S; p += kBlock) {
-        A.r.ids[p] = lids[p];
-        A.r.w[p] = lw[p];
-      }
+    LTRACE(2);
     if (u >= uexp[kMaxUnits]) return;
     const int e = uexp[u];
     uint64_t m = umask[u];
     const bool active = wave * GWG < GK;
     const int g0 = active ? wave * GWG : 0;
+    // the scales first, so that each group's product waits for its own
+    // codes only (loads return in issue order)
     uint4 wq[GWG];
     ScalePack<PG> sc[GWG / PG];
-    const uint8_t* qb = a.gu_q + (size_t)e * a.gu_q_stride + ((size_t)(b * GK + g0) * kWave + lane) * 16;
-#pragma unroll
-    for (int i = 0; i < GWG; ++i) wq[i] = *reinterpret_cast<const uint4*>(qb + (size_t)i * kWave * 16);
     const uint16_t* sb = a.gu_s + (size_t)e * a.gu_s_stride + ((size_t)(b * (GK / PG) + g0 / PG) * kWave + lane) * PG;
 #pragma unroll
     for (int j = 0; j < GWG / PG; ++j) sc[j].load(sb + (size_t)j * kWave * PG);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* qb = a.gu_q + (size_t)e * a.gu_q_stride + ((size_t)(b * GK + g0) * kWave + lane) * 16;
+#pragma unroll
+    for (int i = 0; i < GWG; ++i) wq[i] = *reinterpret_cast<const uint4*>(qb + (size_t)i * kWave * 16);
     const uint32_t magic = bf16_pair_magic();
+    LTRACE(5);
     while (m) {
       const int p = __ffsll((unsigned long long)m) - 1;
       m &= m - 1;
       const int tok = p / a.k;
-      red[wave][lane] = active ? routed_dot<GWG, PG, false>(wq, sc, act + (size_t)tok * a.H, gbias + tok * GK, g0, magic)
+      red[wave][lane] = active ? routed_dot_lds<GWG, PG>(wq, sc, xl + (size_t)tok * (a.H / 2), gbias + tok * GK, g0, magic)
                                : 0.f;
       lds_sync();
       if (wave == 0) {
@@ -432,6 +530,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       }
       lds_sync();
     }
+    LTRACE_WAIT();
+    LTRACE(6);
     return;
   }
 
@@ -458,36 +558,35 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       }
     }
     const uint32_t T = take_tag(A, ev, &tag_lds);
-    if (A.route) gather_keys(A, T, lkeys);
-    select_slots(A, lkeys, topk_lds, lids, lw);
+    if (wave == 0) routing_wave(A, T, r % kSelectors, lane, lids, lw, true);
+    lds_sync();
+    LTRACE(3);
     if (!A.route && r == 0 && tid < a.S && !id_ok(lids[tid], a.E)) atomicOr(a.err, 1);
-    // The routed gate_up stream, which the h records wait for, goes first:
-    // the down rows are needed only once those records land, several
-    // microseconds later, so they are requested kDnLoadDelay after the
-    // routing (realtime ticks of 10 ns; measured: 22.5 us per layer without
-    // the delay, 21.5 with 1.4 to 1.8 us, worse again from 2.5 us).
-    {
-      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      while (__builtin_amdgcn_s_memrealtime() - t0 < kDnLoadDelay) __builtin_amdgcn_s_sleep(1);
-    }
     const int nrec = a.k * GKD;  // (slot, group) records of one token, <= Q * NPQ
     for (int t = 0; t < a.M; ++t) {
-      // this token's down rows of every slot's expert
+      // this token's down rows of every slot's expert: the scales first,
+      // so that the first record's product waits for its own codes only
+      // (loads return in issue order)
       uint4 wd[NPQ];
       uint32_t sdv[NPQ];
 #pragma unroll
       for (int i = 0; i < NPQ; ++i) {
         const int j = q + Q * i, jj = j / GKD, g = j - jj * GKD;
         const int e = j < nrec ? lids[t * a.k + jj] : -1;
-        if (id_ok(e, a.E)) {
-          wd[i] = *reinterpret_cast<const uint4*>(a.dn_q + (size_t)e * a.dn_q_stride +
-                                                  ((size_t)(tile * GKD + g) * kWave + lrow) * 16);
-          sdv[i] = a.dn_s[(size_t)e * a.dn_s_stride + ((size_t)(tile * (GKD / PD) + g / PD) * kWave + lrow) * PD + g % PD];
-        } else {
-          wd[i] = make_uint4(0, 0, 0, 0);
-          sdv[i] = 0;
-        }
+        sdv[i] = id_ok(e, a.E) ? a.dn_s[(size_t)e * a.dn_s_stride + ((size_t)(tile * (GKD / PD) + g / PD) * kWave + lrow) * PD +
+                                        g % PD]
+                               : 0u;
       }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < NPQ; ++i) {
+        const int j = q + Q * i, jj = j / GKD, g = j - jj * GKD;
+        const int e = j < nrec ? lids[t * a.k + jj] : -1;
+        wd[i] = id_ok(e, a.E) ? *reinterpret_cast<const uint4*>(a.dn_q + (size_t)e * a.dn_q_stride +
+                                                               ((size_t)(tile * GKD + g) * kWave + lrow) * 16)
+                              : make_uint4(0, 0, 0, 0);
+      }
+      LTRACE(5);
       // the token's shared h (columns tid + 256 c), which lands long before
       // the routed h: polled first, on its own
       if constexpr (NSC > 0) {
@@ -515,6 +614,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
           __builtin_amdgcn_s_sleep(8);
         }
       }
+      LTRACE(6);
       // the token's h records (thread tid < nrec takes record tid): its
       // exponent word is polled (one word per record and round, so the
       // polls stay light next to the weight stream), then the pairs read
@@ -582,6 +682,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         __builtin_amdgcn_s_sleep(8);
       }
       float acc = 0.f;
+      LTRACE(7);
       const uint32_t magic = fp16_pair_magic();
 #pragma unroll
       for (int i = 0; i < NPQ; ++i) {
@@ -636,6 +737,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         for (int qq = 0; qq < Q; ++qq) y += cred[qq * kDnRows + tid];
         a.out[(size_t)t * a.H + row0 + tid] = f32_to_bf16(y);
       }
+      LTRACE_WAIT();
+      LTRACE(8);
       lds_sync();
     }
   }
@@ -661,16 +764,35 @@ bool layer_variant(const Shape& s, LayerVariant& v) {
   return (ling || tiny) && (v.CWG == 0) == (v.NSC == 0) && s.k * (s.I / kGroup) <= kBlock;
 }
 
+// The workgroups of a launch wait for one another, so the whole grid must be
+// resident at once: the launch is refused (and the caller takes the separate
+// kernels) when the device cannot hold it.
 template <int NI, int GWG, int PG, int CWG, int PD, int NPQ, int NSC, int DG>
 hipError_t run_layer(const LayerArgs& A, size_t lds, hipStream_t st) {
-  hipLaunchKernelGGL((k_layer<NI, GWG, PG, CWG, PD, NPQ, NSC, DG>), dim3(A.g.grid), dim3(kBlock), lds, st, A);
+  auto kern = k_layer<NI, GWG, PG, CWG, PD, NPQ, NSC, DG>;
+  int dev = 0, ncu = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), kBlock, lds) !=
+          hipSuccess)
+    return hipErrorInvalidValue;
+  if ((int64_t)per_cu * ncu < A.g.grid) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(kern, dim3(A.g.grid), dim3(kBlock), lds, st, A);
   return hipGetLastError();
 }
 }  // namespace
 
+#ifdef MOE_LAYER_TRACE
+extern "C" int moe_layer_trace_read(void* dst, size_t bytes) {
+  if (bytes > sizeof(g_layer_trace)) bytes = sizeof(g_layer_trace);
+  return hipMemcpyFromSymbol(dst, HIP_SYMBOL(g_layer_trace), bytes, 0, hipMemcpyDeviceToHost) == hipSuccess ? 0 : -6;
+}
+#endif
+
 bool layer_supported(const Shape& s, int M) {
   LayerVariant v;
-  return (int64_t)M * s.k <= kMaxUnits && (int64_t)M * s.E <= kMaxLayerKeys && layer_variant(s, v);
+  return M <= kLayerMaxTokens && (int64_t)M * s.k <= kMaxUnits && (int64_t)M * s.E <= kMaxLayerKeys &&
+         layer_variant(s, v);
 }
 
 hipError_t launch_layer(const Shape& s, const uint8_t* packed, const PackedLayout& PL, const float* router_w,
@@ -693,13 +815,14 @@ hipError_t launch_layer(const Shape& s, const uint8_t* packed, const PackedLayou
   A.g = layer_roles(s.H, s.E, s.I, s.has_shared, route ? 1 : 0, M, s.k);
   A.epoch = reinterpret_cast<uint32_t*>(ws + L.epoch);
   A.arrive = reinterpret_cast<int32_t*>(ws + L.arrive);
-  A.flags = reinterpret_cast<uint64_t*>(ws + L.flags);
   A.rkeys = reinterpret_cast<uint64_t*>(ws + L.rkeys);
+  A.rrec = reinterpret_cast<uint64_t*>(ws + L.rrec);
   A.hval = reinterpret_cast<uint64_t*>(ws + L.hval);
   A.hmeta = reinterpret_cast<uint64_t*>(ws + L.hmeta);
   A.hsh = reinterpret_cast<uint64_t*>(ws + L.hsh);
-  // router keys (routing in the launch), then the group corrections
-  const size_t lds = (size_t)M * ((route ? s.E : 0) + s.H / kGroup) * 4;
+  // router keys (routing in the launch), then the staged tokens and their
+  // group corrections
+  const size_t lds = ((size_t)M * (route ? s.E : 0) + (size_t)M * (s.H / 2 + s.H / kGroup)) * 4;
 #define LAYER_CASE(NI_, GWG_, PG_, CWG_, PD_, NPQ_, NSC_, DG_)                                              \
   if (v.NI == NI_ && v.GWG == GWG_ && v.PG == PG_ && v.CWG == CWG_ && v.PD == PD_ && v.NPQ == NPQ_ &&       \
       v.NSC == NSC_ && v.DG == DG_)                                                                          \

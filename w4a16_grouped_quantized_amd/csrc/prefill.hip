@@ -668,7 +668,7 @@ struct TopkArgs {
 // k largest logits, ties to the lower id, softmax over them) on logits that a
 // previous launch produced.
 __global__ __launch_bounds__(kBlock) void k_topk_rows(const TopkArgs a) {
-  __shared__ __align__(16) int lds_all[kWavesPerBlock][3 * kMaxTopK];
+  __shared__ __align__(16) int lds_all[kWavesPerBlock][kTopkLdsInts];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * kWavesPerBlock + wave;
   if (t >= a.M) return;

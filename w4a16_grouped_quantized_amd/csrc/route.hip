@@ -18,7 +18,7 @@ namespace moe {
 template <int NI>
 __global__ __launch_bounds__(kBlock) void k_route(const RouteArgs a) {
   __shared__ int flag;
-  __shared__ __align__(16) int topk_lds[kWavesPerBlock][3 * kMaxTopK];
+  __shared__ __align__(16) int topk_lds[kWavesPerBlock][kTopkLdsInts];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   router_row<NI>(a, blockIdx.x * kWavesPerBlock + wave, lane, blockIdx.x == 0 && wave == 0);
   if (!arrive_last_tree(a.cnt, blockIdx.x, gridDim.x, &flag)) return;

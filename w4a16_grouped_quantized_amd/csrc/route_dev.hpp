@@ -61,8 +61,9 @@ __device__ __forceinline__ uint32_t kth_largest_lane_prefix(uint32_t key, int k)
 // lane + 64*j; absent entries are not present).  Lanes < k return the id and
 // softmax weight of rank `lane` (the weight only with want_w; 0 otherwise).
 constexpr int kTopkEPL = kMaxExperts / kWave;
-__device__ __forceinline__ void topk_select(const uint32_t (&key)[kTopkEPL], const bool (&present)[kTopkEPL], int k,
-                                            int lane, int* lds, int& out_id, float& out_w, bool want_w = true) {
+__device__ __forceinline__ void topk_select_general(const uint32_t (&key)[kTopkEPL], const bool (&present)[kTopkEPL],
+                                                    int k, int lane, int* lds, int& out_id, float& out_w,
+                                                    bool want_w = true) {
   constexpr int EPL = kTopkEPL;
   uint32_t lmax = 0;
 #pragma unroll
@@ -156,6 +157,116 @@ __device__ __forceinline__ void topk_select(const uint32_t (&key)[kTopkEPL], con
     sum = wave_sum(ex);
   }
   out_w = ex / sum;
+}
+
+// The same selection for k <= 8, in few dependent steps (the general one
+// spends most of its time in serialised ballot and LDS round trips).
+//  1. Threshold: the smallest of the eight group maxima (lanes 8g .. 8g+7,
+//     all their keys): every group holds a key at or above it, so at least
+//     eight keys reach it (about twelve for N(0, 1) logits).  Lane maxima
+//     with max3, group maxima with three DPP steps, their minimum on the
+//     scalar unit.
+//  2. The candidates (keys at or above it) go to LDS as 64-bit composites
+//     (key << 32 | 0xFFFF - id): the larger composite is the larger key,
+//     then the lower id.  All eight ballots are taken before any position,
+//     and every lane writes (non-candidates to a slot of their own), so no
+//     step waits on the previous one.  More than 64 candidates (heavy
+//     ties): the general selection.
+//  3. Candidate c's rank is the number of larger composites, read sixteen
+//     at a time; ranks below k are the result, in order.
+//  4. The weights' sum runs over the same pairs as in the general selection
+//     (lanes 1, 2 and 4 apart), through DPP instead of LDS shuffles; the
+//     sums are the same bits.
+// The LDS area takes kTopkLdsInts ints per wavefront.
+constexpr int kTopkLdsInts = 288;  // 128 candidate slots + 16 result slots, 8 bytes each
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+__device__ __forceinline__ void topk_select_small(const uint32_t (&key)[kTopkEPL], const bool (&present)[kTopkEPL], int k,
+                                                  int lane, int* lds, int& out_id, float& out_w, bool want_w = true) {
+  constexpr int EPL = kTopkEPL;
+  uint32_t kv[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) kv[j] = present[j] ? key[j] : 0u;
+  uint32_t m = kv[0];
+#pragma unroll
+  for (int j = 1; j < EPL; ++j) m = max(m, kv[j]);
+  m = max(m, dpp_u32<kDppXor1>(m));
+  m = max(m, dpp_u32<kDppXor2>(m));
+  m = max(m, dpp_u32<kDppHalfMirror>(m));
+  uint32_t gmax[8];
+#pragma unroll
+  for (int g = 0; g < 8; ++g) gmax[g] = (uint32_t)__builtin_amdgcn_readlane((int)m, 8 * g);
+  const uint32_t thr = min(min(min(gmax[0], gmax[1]), min(gmax[2], gmax[3])), min(min(gmax[4], gmax[5]), min(gmax[6], gmax[7])));
+  bool c[EPL];
+  uint64_t b[EPL];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    c[j] = present[j] && kv[j] >= thr;
+    b[j] = __ballot(c[j]);
+  }
+  int pre[EPL + 1];
+  pre[0] = 0;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) pre[j + 1] = pre[j] + __popcll(b[j]);
+  const int C = pre[EPL];
+  if (C > kWave) {  // heavy ties: the general selection
+    topk_select_general(key, present, k, lane, lds, out_id, out_w, want_w);
+    return;
+  }
+  uint64_t* cand = reinterpret_cast<uint64_t*>(lds);  // [0, 64) candidates, [64, 128) discarded writes
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b[j] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b[j], 0u));
+    cand[c[j] ? pre[j] + below : kWave + lane] = ((uint64_t)kv[j] << 32) | (uint32_t)(0xFFFF - (lane + kWave * j));
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  const uint64_t mine = cand[lane];
+  int rank = 0;
+  for (int i0 = 0; i0 < C; i0 += 16) {
+    ulonglong2 v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = reinterpret_cast<const ulonglong2*>(cand)[i0 / 2 + q];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      rank += (i0 + 2 * q < C && v[q].x > mine) ? 1 : 0;
+      rank += (i0 + 2 * q + 1 < C && v[q].y > mine) ? 1 : 0;
+    }
+  }
+  uint64_t* res = cand + 2 * kWave;
+  if (lane < C && rank < k) res[rank] = mine;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+  const uint64_t r = res[lane < k ? lane : 0];
+  out_id = 0xFFFF - (int)(uint32_t)(r & 0xFFFFu);
+  if (!want_w) {
+    out_w = 0.f;
+    return;
+  }
+  const float v = lane < k ? key_value((uint32_t)(r >> 32)) : 0.f;
+  const float vmax = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 0));
+  const float ex = lane < k ? expf(v - vmax) : 0.f;
+  float sum = ex + dpp_f32<kDppXor1>(ex);
+  sum = sum + dpp_f32<kDppXor2>(sum);
+  sum = sum + dpp_f32<kDppHalfMirror>(sum);
+  out_w = ex / sum;
+}
+
+// The top-k selection every path uses: the small-k form for k <= 8, else
+// the general one.  lds: kTopkLdsInts ints of this wavefront.
+__device__ __forceinline__ void topk_select(const uint32_t (&key)[kTopkEPL], const bool (&present)[kTopkEPL], int k,
+                                            int lane, int* lds, int& out_id, float& out_w, bool want_w = true) {
+  if (k <= 8) topk_select_small(key, present, k, lane, lds, out_id, out_w, want_w);
+  else topk_select_general(key, present, k, lane, lds, out_id, out_w, want_w);
 }
 
 // Top-k of logits[t][0..E) (fp32, written by the other workgroups of the
