@@ -24,8 +24,9 @@
  *    moe_get_device_error) and launch fixed-size grids, so they may be
  *    captured into a HIP graph.
  *  - The caller owns every buffer.  The library keeps no mutable global
- *    state; calls that share one workspace must be stream-ordered (calls on
- *    different workspaces may run concurrently).
+ *    state other than the static workspace of moe_layer_w4a16_noalloc; calls
+ *    that share one workspace must be stream-ordered (calls on different
+ *    workspaces may run concurrently).
  *  - Arguments are checked before anything is launched; a failed check
  *    returns a negative moe_status and launches nothing.  There is no
  *    fallback path: an unsupported shape is an error.
@@ -184,6 +185,29 @@ int moe_layer_w4a16(const moe_config* cfg /* host */, const float* router_w, con
                     const uint16_t* x, int32_t M, uint32_t flags, uint16_t* x_norm,
                     int32_t* topk_ids, float* topk_w, uint16_t* out,
                     void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of the library's own workspace used by moe_layer_w4a16_noalloc. */
+#define MOE_NOALLOC_WS_BYTES ((size_t)16 << 20)
+
+/* moe_layer_w4a16 for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, results and errors as
+ * moe_layer_w4a16 minus ws / ws_bytes: the workspace is a static device array
+ * of MOE_NOALLOC_WS_BYTES inside the library, one per GPU, zero at load and
+ * held until the process ends; its address on the current device is looked
+ * up once (no allocation, here or later).  A call whose workspace need
+ * (moe_workspace_size of its M) exceeds that size returns MOE_ERR_WORKSPACE
+ * and launches nothing; for the Ling-3.0-flash shape that is M > 90.  Every
+ * call on one GPU shares that GPU's array and finds the last call's contents
+ * (the layer's hand-off words carry a per-call tag and its counters return
+ * to zero at the end of each call, so nothing needs clearing between calls):
+ * calls that overlap on one GPU (different streams, or another thread) race
+ * and must be serialised by the caller.  The routing is computed inside the
+ * call, so the expert ids are always in range; the device error word of this
+ * workspace is not exposed.  The caller still owns every input and output. */
+int moe_layer_w4a16_noalloc(const moe_config* cfg /* host */, const float* router_w, const void* packed,
+                            const uint16_t* x, int32_t M, uint32_t flags, uint16_t* x_norm,
+                            int32_t* topk_ids, float* topk_w, uint16_t* out, void* stream);
 
 /* The two stages of moe_forward_w4a16 (the gate_up/SiLU half and the
  * down/combine half of the expert FFNs moe_forward_w4a16 cites), for callers

@@ -149,3 +149,22 @@ def test_read_probe_validation(lib):
     assert lib.moe_probe_read(a, 65, a, 8, None) == -3
     assert lib.moe_probe_read(a, 64, a, 0, None) == -2
     assert lib.moe_probe_read(a, 0, a, 8, None) == 0
+
+
+def test_noalloc_limits_checked_on_the_host(lib):
+    """moe_layer_w4a16_noalloc: the static workspace size the binding uses is
+    the header's, and sizes are refused before the device is touched."""
+    hdr = open(HEADER).read()
+    m = re.search(r"#define MOE_NOALLOC_WS_BYTES \(\(size_t\)(\d+) << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.MOE_NOALLOC_WS_BYTES
+    cfg = B.config(synth.LING)
+    a = ctypes.c_void_p(0x10000)
+    big = 1
+    while lib.moe_workspace_size(ctypes.byref(cfg), big) <= B.MOE_NOALLOC_WS_BYTES:
+        big += 1
+    assert big > 64
+    args = (0, None, a, a, a, None)  # flags, x_norm, ids, weights, out, stream
+    assert lib.moe_layer_w4a16_noalloc(ctypes.byref(cfg), a, a, a, big, *args) == B.MOE_ERR_WORKSPACE
+    assert lib.moe_layer_w4a16_noalloc(ctypes.byref(cfg), a, a, a, -1, *args) == -2
+    assert lib.moe_layer_w4a16_noalloc(ctypes.byref(cfg), a, a, a, 0, *args) == 0
+    assert lib.moe_layer_w4a16_noalloc(None, a, a, a, 1, *args) == -1

@@ -18,6 +18,9 @@ LIB_PATH = os.path.join(_HERE, "libmoe_w4a16.so")
 
 MOE_F_INPUT_RMSNORM = 0x1
 MOE_F_ONE_LAUNCH = 0x2
+MOE_ERR_WORKSPACE = -4
+# bytes of the static workspace of moe_layer_w4a16_noalloc (MOE_NOALLOC_WS_BYTES)
+MOE_NOALLOC_WS_BYTES = 16 << 20
 
 MOE_OK = 0
 STATUS_NAMES = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_ALIGN",
@@ -27,7 +30,8 @@ STATUS_NAMES = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_E
 # Every symbol include/moe_w4a16.h declares.
 EXPORTS = ("moe_packed_size", "moe_pack_weights", "moe_workspace_size", "moe_workspace_init",
            "moe_route", "moe_forward_w4a16", "moe_layer_w4a16", "moe_gate_up_w4a16", "moe_down_w4a16", "moe_permute",
-           "moe_get_device_error", "moe_status_string", "moe_build_info", "moe_probe_read")
+           "moe_get_device_error", "moe_status_string", "moe_build_info", "moe_probe_read",
+           "moe_layer_w4a16_noalloc")
 
 
 class MoeError(RuntimeError):
@@ -73,6 +77,8 @@ def lib() -> ctypes.CDLL:
             L.moe_forward_w4a16.argtypes = [cfgp, _P, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t, _P]
             L.moe_layer_w4a16.argtypes = [cfgp, _P, _P, _P, ctypes.c_int32, ctypes.c_uint32, _P, _P, _P, _P, _P,
                                           ctypes.c_size_t, _P]
+            L.moe_layer_w4a16_noalloc.argtypes = [cfgp, _P, _P, _P, ctypes.c_int32, ctypes.c_uint32, _P, _P, _P,
+                                                  _P, _P]
             L.moe_gate_up_w4a16.argtypes = [cfgp, _P, _P, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]
             L.moe_down_w4a16.argtypes = [cfgp, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t, _P]
             L.moe_permute.argtypes = [cfgp, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t, _P]
@@ -152,6 +158,14 @@ def layer(cfg, router_w, packed, x, topk_ids, topk_w, out, ws, flags: int = 0, x
     _check("moe_layer_w4a16", lib().moe_layer_w4a16(ctypes.byref(cfg), _ptr(router_w), _ptr(packed), _ptr(x), M,
                                                     flags, _ptr(x_norm), _ptr(topk_ids), _ptr(topk_w), _ptr(out),
                                                     _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def layer_noalloc(cfg, router_w, packed, x, topk_ids, topk_w, out, flags: int = 0, x_norm=None, stream=None):
+    """moe_layer_w4a16 on the library's own static workspace (no allocation)."""
+    M = x.shape[0]
+    _check("moe_layer_w4a16_noalloc",
+           lib().moe_layer_w4a16_noalloc(ctypes.byref(cfg), _ptr(router_w), _ptr(packed), _ptr(x), M, flags,
+                                         _ptr(x_norm), _ptr(topk_ids), _ptr(topk_w), _ptr(out), _stream(stream)))
 
 
 def gate_up(cfg, packed, x, topk_ids, ws, stream=None):

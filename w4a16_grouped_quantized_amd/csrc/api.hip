@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "launch.hpp"
 
 using namespace moe;
@@ -46,6 +48,31 @@ int check_cfg(const moe_config* c, Shape* s) {
 }
 
 int launched(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+// The library's own workspace for moe_layer_w4a16_noalloc: one copy per GPU,
+// zero at load like every static, held until the process ends.  Host code
+// never passes the array's name to a kernel (on the host it names a stand-in,
+// not device memory); it uses the address hipGetSymbolAddress gives on each
+// device.
+constexpr size_t kScratchBytes = MOE_NOALLOC_WS_BYTES;
+constexpr int kMaxScratchDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The current device's copy of scratch (nullptr if its address cannot be had).
+void* scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
 
 }  // namespace
 
@@ -221,6 +248,22 @@ int moe_layer_w4a16(const moe_config* cfg, const float* router_w, const void* pa
   rc = moe_route(cfg, router_w, x, M, flags & MOE_F_INPUT_RMSNORM, x_norm, topk_ids, topk_w, ws, ws_bytes, stream);
   if (rc != MOE_OK) return rc;
   return moe_forward_w4a16(cfg, packed, rms ? x_norm : x, M, topk_ids, topk_w, out, ws, ws_bytes, stream);
+}
+
+int moe_layer_w4a16_noalloc(const moe_config* cfg, const float* router_w, const void* packed, const uint16_t* x,
+                            int32_t M, uint32_t flags, uint16_t* x_norm, int32_t* topk_ids, float* topk_w,
+                            uint16_t* out, void* stream) {
+  if (M == 0) return MOE_OK;
+  // the sizes are checked before the set-up (and again by moe_layer_w4a16)
+  Shape s;
+  const int rc = check_cfg(cfg, &s);
+  if (rc != MOE_OK) return rc;
+  if (M < 0) return MOE_ERR_SHAPE;
+  if (moe_workspace_size(cfg, M) > kScratchBytes) return MOE_ERR_WORKSPACE;
+  void* ws = scratch_on_current_device();
+  if (!ws) return MOE_ERR_LAUNCH;
+  return moe_layer_w4a16(cfg, router_w, packed, x, M, flags, x_norm, topk_ids, topk_w, out, ws, kScratchBytes,
+                         stream);
 }
 
 int moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t M, int32_t* counts, int32_t* offsets,
