@@ -22,6 +22,17 @@
  * nibble holding the even k, groups of 32 along K, the shared expert added
  * with weight 1, and an RMSNorm with unit gain between stacked layers.
  *
+ * The further formats follow:
+ *  - bpdata.com article, model section and "Optimalizáció 1": the FP4
+ *    checkpoint served with MXFP4 MoE kernels (E2M1 codes with one E8M0
+ *    scale per block of 32, the OCP MX format);
+ *  - same article, "Optimalizáció 2": the BF16 LM head (2,560 -> 157,184)
+ *    turned into FP8 when the head is assembled, halving its read volume;
+ *    reading: E4M3 with one float32 scale per row, amax / 448;
+ *  - vLLM recipe page, Overview and Prerequisites: the serialized block-FP8
+ *    checkpoint with BF16 compute; reading: E4M3 codes with one float32
+ *    scale per 128 x 128 block.
+ *
  * All pointers are host pointers.  Arrays are row-major and contiguous.
  * bf16 values travel as uint16_t bit patterns.
  */
@@ -100,6 +111,46 @@ int oracle_rmsnorm(const uint16_t* y, int32_t M, int32_t H, double eps, uint16_t
 
 /* Number of OpenMP threads the oracle uses (1 without OpenMP). */
 int oracle_num_threads(void);
+
+
+/* ---- further weight formats ------------------------------------------- */
+/* FP8 E4M3 (OCP): bias 7, no infinities, S.1111.111 NaN, largest 448. */
+double oracle_e4m3_to_f64(uint8_t c);
+/* Nearest finite E4M3 code (ties to the even mantissa, saturating at 448). */
+uint8_t oracle_f32_to_e4m3(float v);
+/* Online FP8 LM head: per-row scale amax/448 and E4M3 codes of w/scale
+ * (float32 arithmetic); w [V][H] bf16 -> q [V][H], s [V]. */
+int oracle_lmhead_quantize(const uint16_t* w, int32_t V, int32_t H, uint8_t* q, float* s);
+/* out [M][V] = s[v] * sum_h e4m3(q[v][h]) * x[t][h], in double. */
+int oracle_lmhead_gemv_fp8(const uint8_t* q, const float* s, int32_t V, int32_t H, const uint16_t* x,
+                           int32_t M, double* out);
+/* out [M][V] = sum_h w[v][h] * x[t][h] for a BF16 head, in double. */
+int oracle_lmhead_gemv_bf16(const uint16_t* w, int32_t V, int32_t H, const uint16_t* x, int32_t M,
+                            double* out);
+/* E2M1 (OCP 4-bit float) code -> value; E8M0 scale code -> 2^(c-127). */
+double oracle_e2m1_to_f64(uint8_t c);
+double oracle_e8m0_to_f64(uint8_t c);
+
+/* Routed-expert weight formats. */
+enum { ORACLE_FMT_INT4_G32 = 0, ORACLE_FMT_MXFP4 = 1, ORACLE_FMT_FP8_BLOCK = 2 };
+/* Routed experts in format fmt (per expert, as in oracle_experts):
+ *   INT4_G32   q [N][K/2] nibbles, s bf16 [N][K/32]
+ *   MXFP4      q [N][K/2] E2M1 nibbles, s uint8 E8M0 [N][K/32]
+ *   FP8_BLOCK  q [N][K] E4M3 codes, s float32 [ceil(N/128)][ceil(K/128)] */
+typedef struct {
+  int32_t fmt;
+  const uint8_t* const* w13_q;
+  const void* const* w13_s;
+  const uint8_t* const* w2_q;
+  const void* const* w2_s;
+  const uint16_t* sh_w13;
+  const uint16_t* sh_w2;
+} oracle_experts_fmt;
+/* Dequantise an N x K matrix of format fmt into W [N][K]. */
+int oracle_dequant_fmt(int32_t fmt, const uint8_t* q, const void* s, int32_t N, int32_t K, double* W);
+/* oracle_forward with routed experts in format ex->fmt (shared expert BF16). */
+int oracle_forward_fmt(const oracle_cfg* cfg, const oracle_experts_fmt* ex, const uint16_t* x, int32_t M,
+                       const int32_t* ids, const double* w, double* out);
 
 #ifdef __cplusplus
 }

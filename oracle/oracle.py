@@ -51,6 +51,16 @@ class _Experts(ctypes.Structure):
                 ("sh_w13", _P), ("sh_w2", _P)]
 
 
+class _ExpertsFmt(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("w13_q", _P), ("w13_s", _P), ("w2_q", _P), ("w2_s", _P),
+                ("sh_w13", _P), ("sh_w2", _P)]
+
+
+# routed-expert weight formats (oracle_forward_fmt)
+FMT_INT4_G32, FMT_MXFP4, FMT_FP8_BLOCK = 0, 1, 2
+_SCALE_DTYPE = {FMT_INT4_G32: np.uint16, FMT_MXFP4: np.uint8, FMT_FP8_BLOCK: np.float32}
+
+
 def lib():
     global _lib
     with _lock:
@@ -72,6 +82,20 @@ def lib():
             L.oracle_permute.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
             L.oracle_rmsnorm.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, ctypes.c_double, _P]
             L.oracle_num_threads.restype = ctypes.c_int
+            L.oracle_e4m3_to_f64.restype = ctypes.c_double
+            L.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+            L.oracle_f32_to_e4m3.restype = ctypes.c_uint8
+            L.oracle_f32_to_e4m3.argtypes = [ctypes.c_float]
+            L.oracle_lmhead_quantize.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, _P, _P]
+            L.oracle_lmhead_gemv_fp8.argtypes = [_P, _P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P]
+            L.oracle_lmhead_gemv_bf16.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P]
+            L.oracle_e2m1_to_f64.restype = ctypes.c_double
+            L.oracle_e2m1_to_f64.argtypes = [ctypes.c_uint8]
+            L.oracle_e8m0_to_f64.restype = ctypes.c_double
+            L.oracle_e8m0_to_f64.argtypes = [ctypes.c_uint8]
+            L.oracle_dequant_fmt.argtypes = [ctypes.c_int32, _P, _P, ctypes.c_int32, ctypes.c_int32, _P]
+            L.oracle_forward_fmt.argtypes = [ctypes.POINTER(_Cfg), ctypes.POINTER(_ExpertsFmt), _P,
+                                             ctypes.c_int32, _P, _P, _P]
             _lib = L
         return _lib
 
@@ -216,3 +240,99 @@ def rmsnorm(y_bits, eps: float = 1e-6):
     if lib().oracle_rmsnorm(_ptr(y), M, H, eps, _ptr(out)) != 0:
         raise ValueError("oracle_rmsnorm: bad arguments")
     return out
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    c = _c(codes, np.uint8)
+    return np.array([lib().oracle_e4m3_to_f64(int(v)) for v in c.ravel()]).reshape(c.shape)
+
+
+def f32_to_e4m3(v) -> np.ndarray:
+    v = _c(v, np.float32)
+    return np.array([lib().oracle_f32_to_e4m3(float(a)) for a in v.ravel()], np.uint8).reshape(v.shape)
+
+
+def e2m1_to_f64(codes) -> np.ndarray:
+    c = _c(codes, np.uint8)
+    return np.array([lib().oracle_e2m1_to_f64(int(v)) for v in c.ravel()]).reshape(c.shape)
+
+
+def e8m0_to_f64(codes) -> np.ndarray:
+    c = _c(codes, np.uint8)
+    return np.array([lib().oracle_e8m0_to_f64(int(v)) for v in c.ravel()]).reshape(c.shape)
+
+
+def lmhead_quantize(w_bits):
+    """w bf16 [V][H] -> (q uint8 E4M3 [V][H], s float32 [V])."""
+    w = _c(w_bits, np.uint16)
+    V, H = w.shape
+    q = np.empty((V, H), np.uint8)
+    sc = np.empty(V, np.float32)
+    if lib().oracle_lmhead_quantize(_ptr(w), V, H, _ptr(q), _ptr(sc)) != 0:
+        raise ValueError("oracle_lmhead_quantize: bad arguments")
+    return q, sc
+
+
+def lmhead_gemv_fp8(q, sc, x_bits) -> np.ndarray:
+    q, sc = _c(q, np.uint8), _c(sc, np.float32)
+    V, H = q.shape
+    x = _c(x_bits, np.uint16).reshape(-1, H)
+    out = np.empty((x.shape[0], V), np.float64)
+    if lib().oracle_lmhead_gemv_fp8(_ptr(q), _ptr(sc), V, H, _ptr(x), x.shape[0], _ptr(out)) != 0:
+        raise ValueError("oracle_lmhead_gemv_fp8: bad arguments")
+    return out
+
+
+def lmhead_gemv_bf16(w_bits, x_bits) -> np.ndarray:
+    w = _c(w_bits, np.uint16)
+    V, H = w.shape
+    x = _c(x_bits, np.uint16).reshape(-1, H)
+    out = np.empty((x.shape[0], V), np.float64)
+    if lib().oracle_lmhead_gemv_bf16(_ptr(w), V, H, _ptr(x), x.shape[0], _ptr(out)) != 0:
+        raise ValueError("oracle_lmhead_gemv_bf16: bad arguments")
+    return out
+
+
+def dequant_fmt(fmt: int, q, s, N: int, K: int) -> np.ndarray:
+    q, s = _c(q, np.uint8), _c(s, _SCALE_DTYPE[fmt])
+    W = np.empty((N, K), np.float64)
+    if lib().oracle_dequant_fmt(fmt, _ptr(q), _ptr(s), N, K, _ptr(W)) != 0:
+        raise ValueError("oracle_dequant_fmt: bad arguments")
+    return W
+
+
+def forward_fmt(shape, fmt: int, experts, x, ids, w):
+    """oracle_forward with the routed experts in format fmt: experts maps
+    w13_q/w13_s/w2_q/w2_s to {expert id: array} (or [E]-leading arrays) and
+    holds sh_w13/sh_w2.  Returns (out float64 [M][H], bad-id count)."""
+    E = shape.n_experts
+    x = _c(x, np.uint16).reshape(-1, shape.hidden)
+    ids = _c(ids, np.int32).reshape(x.shape[0], shape.top_k)
+    w = _c(w, np.float64).reshape(x.shape[0], shape.top_k)
+    keep = []
+
+    def table(name, dtype):
+        src = experts[name]
+        arr = (ctypes.c_void_p * E)()
+        for e in range(E):
+            a = src.get(e) if isinstance(src, dict) else src[e]
+            if a is not None:
+                a = _c(a, dtype)
+                keep.append(a)
+                arr[e] = a.ctypes.data
+        keep.append(arr)
+        return ctypes.cast(arr, ctypes.c_void_p)
+
+    sh13, sh2 = experts.get("sh_w13"), experts.get("sh_w2")
+    sh13 = None if sh13 is None else _c(sh13, np.uint16)
+    sh2 = None if sh2 is None else _c(sh2, np.uint16)
+    sd = _SCALE_DTYPE[fmt]
+    ex = _ExpertsFmt(fmt, table("w13_q", np.uint8), table("w13_s", sd), table("w2_q", np.uint8),
+                     table("w2_s", sd), _ptr(sh13), _ptr(sh2))
+    out = np.empty((x.shape[0], shape.hidden), np.float64)
+    c = _cfg(shape)
+    rc = lib().oracle_forward_fmt(ctypes.byref(c), ctypes.byref(ex), _ptr(x), x.shape[0], _ptr(ids), _ptr(w),
+                                  _ptr(out))
+    if rc < 0:
+        raise ValueError(f"oracle_forward_fmt: error {rc}")
+    return out, rc

@@ -1,6 +1,6 @@
 """Mutation check of the oracle's pins: each plausible slip planted into a
 scratch copy of oracle/moe_oracle.c must make at least one pin in
-test_oracle_pins.py fail.
+test_oracle_pins.py or test_oracle_formats.py fail.
 
 For every mutation the copy is compiled with the oracle's own flags, and the
 pin suite runs in a child process that loads that build (MOE_ORACLE_LIB).  An
@@ -17,7 +17,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "moe_oracle.c")
 HDR = os.path.join(ROOT, "oracle", "moe_oracle.h")
-PINS = os.path.join(ROOT, "tests", "test_oracle_pins.py")
+PINS = [os.path.join(ROOT, "tests", "test_oracle_pins.py"), os.path.join(ROOT, "tests", "test_oracle_formats.py")]
 
 # (name, exact text in moe_oracle.c, replacement): each one a slip that a
 # reader of the pages could plausibly make.
@@ -56,6 +56,21 @@ MUTATIONS = [
     ("RMS multiplies", "oracle_bf16_to_f64(y[(int64_t)t * H + h]) / d)", "oracle_bf16_to_f64(y[(int64_t)t * H + h]) * d)"),
     ("bf16 subnormal step", "if (qexp < -133) qexp = -133;", "if (qexp < -126) qexp = -126;"),
     ("bf16 ties away from zero", "r = nearbyint(ldexp(a, -qexp));", "r = floor(ldexp(a, -qexp) + 0.5);"),
+    ("E4M3 exponent bias 8", "ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)"),
+    ("E4M3 subnormal step", "ldexp((double)m, -9)", "ldexp((double)m, -10)"),
+    ("E4M3 ties to odd", "(d == best_d && (c & 1) == 0 && (best & 1) == 1)", "(d == best_d && (c & 1) == 1 && (best & 1) == 0)"),
+    ("E4M3 overflow to NaN", "if (a >= 448.0) return (uint8_t)(sign | 0x7E);", "if (a >= 448.0) return (uint8_t)(sign | 0x7F);"),
+    ("LM head scale 240", "amax > 0.0f ? amax / 448.0f : 1.0f", "amax > 0.0f ? amax / 240.0f : 1.0f"),
+    ("LM head multiplies by the scale", "(float)oracle_bf16_to_f64(w[(int64_t)v * H + h]) / sv)",
+     "(float)oracle_bf16_to_f64(w[(int64_t)v * H + h]) * sv)"),
+    ("LM head product drops the scale", "out[(int64_t)t * V + v] = (double)s[v] * acc;", "out[(int64_t)t * V + v] = acc;"),
+    ("E2M1 subnormal 0.25", "e == 0 ? 0.5 * m :", "e == 0 ? 0.25 * m :"),
+    ("E2M1 exponent bias 0", "ldexp(1.0 + m / 2.0, e - 1)", "ldexp(1.0 + m / 2.0, e)"),
+    ("E8M0 bias 128", "ldexp(1.0, (int)c - 127)", "ldexp(1.0, (int)c - 128)"),
+    ("MXFP4 scale group shifted", "oracle_e8m0_to_f64(((const uint8_t*)s)[(int64_t)n * (K / 32) + k / 32])",
+     "oracle_e8m0_to_f64(((const uint8_t*)s)[(int64_t)n * (K / 32) + (k / 32 + 1) % (K / 32)])"),
+    ("FP8 block of 64 columns", "sf[(int64_t)(n / 128) * kb + k / 128]", "sf[(int64_t)(n / 128) * kb + (k / 64) % kb]"),
+    ("format ignored by the forward", "expert_fmt(cfg, ex->fmt, ex->w13_q[e]", "expert_fmt(cfg, ORACLE_FMT_INT4_G32, ex->w13_q[e]"),
 ]
 
 
@@ -76,7 +91,7 @@ def _build(src_text, d):
 
 def _pins_pass(lib):
     env = dict(os.environ, MOE_ORACLE_LIB=lib, OMP_NUM_THREADS="4")
-    r = subprocess.run([sys.executable, "-m", "pytest", PINS, "-x", "-q", "-p", "no:cacheprovider"],
+    r = subprocess.run([sys.executable, "-m", "pytest", *PINS, "-x", "-q", "-p", "no:cacheprovider"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     return r.returncode == 0, r.stdout[-400:]
 

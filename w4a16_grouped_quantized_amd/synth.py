@@ -43,7 +43,8 @@ import numpy as np
 __all__ = [
     "LayerShape", "TINY", "LING", "Layer", "make_layer", "make_expert",
     "make_tokens", "bf16_bits", "bf16_bits_to_f32", "pack_codes",
-    "unpack_codes_reference_free",
+    "unpack_codes_reference_free", "FMT_INT4_G32", "FMT_MXFP4", "FMT_FP8_BLOCK",
+    "FmtLayer", "make_layer_fmt", "make_lmhead", "LM_VOCAB",
 ]
 
 
@@ -190,3 +191,109 @@ def make_tokens(shape: LayerShape, seed: int, M: int) -> np.ndarray:
     d, _ = _seeds(seed, shape)
     rng = np.random.Generator(np.random.PCG64(d["x"]))
     return bf16_bits(rng.standard_normal((M, shape.hidden)))
+
+
+# ---------------------------------------------------------------- other formats
+#
+# Routed experts in the two other formats the pages serve, for the same
+# layer shapes: MXFP4 (bpdata.com article, model section and "Optimalizáció
+# 1": the FP4 checkpoint run with MXFP4 MoE kernels) and block FP8 (vLLM
+# recipe page, Overview / Prerequisites: the serialized block-FP8
+# checkpoint).  The codes are drawn directly in the storage format:
+#
+#   MXFP4      w13_q uint8 [E][2I][H/2], w2_q [E][H][I/2]: E2M1 nibbles (low
+#              nibble = even k), each uniform over the 16 codes;
+#              w13_s uint8 [E][2I][H/32], w2_s [E][H][I/32]: E8M0 scales,
+#              uniform over 118..124 (2^-9 .. 2^-3);
+#   FP8_BLOCK  w13_q uint8 [E][2I][H], w2_q [E][H][I]: E4M3 codes, uniform
+#              over the 254 finite codes; w13_s float32
+#              [E][ceil(2I/128)][ceil(H/128)], w2_s [E][ceil(H/128)][ceil(I/128)]:
+#              |N(0,1)| * 3e-4 + 1e-5 per 128 x 128 block.
+#
+# The router and the shared expert are those of make_layer(shape, seed).
+# Format streams: SeedSequence([seed, fmt]).spawn(4) in the order
+# [w13_q, w13_s, w2_q, w2_s], each split per expert (child.spawn(E)).
+
+FMT_INT4_G32, FMT_MXFP4, FMT_FP8_BLOCK = 0, 1, 2
+
+
+@dataclasses.dataclass
+class FmtLayer:
+    shape: LayerShape
+    seed: int
+    fmt: int
+    router_w: np.ndarray
+    w13_q: np.ndarray
+    w13_s: np.ndarray
+    w2_q: np.ndarray
+    w2_s: np.ndarray
+    sh_w13: np.ndarray | None
+    sh_w2: np.ndarray | None
+
+
+def _fp8_codes(rng, shape):
+    r = rng.integers(0, 254, size=shape, dtype=np.uint8)
+    return np.where(r < 127, r, r + 1).astype(np.uint8)  # skips 0x7F; 0xFF is never reached
+
+
+def make_layer_fmt(shape: LayerShape, seed: int, fmt: int, threads: int = 8) -> FmtLayer:
+    """Layer `seed` with its routed experts in format fmt (MXFP4 or FP8_BLOCK)."""
+    if fmt not in (FMT_MXFP4, FMT_FP8_BLOCK):
+        raise ValueError("fmt must be FMT_MXFP4 or FMT_FP8_BLOCK")
+    H, I, E, G = shape.hidden, shape.inter, shape.n_experts, shape.group_size
+    d, _ = _seeds(seed, shape)
+    router = (np.random.Generator(np.random.PCG64(d["router"])).standard_normal((E, H)) * 0.02).astype(np.float32)
+    kids = [k.spawn(E) for k in np.random.SeedSequence([seed, fmt]).spawn(4)]
+    if fmt == FMT_MXFP4:
+        w13_q = np.empty((E, 2 * I, H // 2), np.uint8)
+        w2_q = np.empty((E, H, I // 2), np.uint8)
+        w13_s = np.empty((E, 2 * I, H // G), np.uint8)
+        w2_s = np.empty((E, H, I // G), np.uint8)
+    else:
+        b = lambda n: (n + 127) // 128
+        w13_q = np.empty((E, 2 * I, H), np.uint8)
+        w2_q = np.empty((E, H, I), np.uint8)
+        w13_s = np.empty((E, b(2 * I), b(H)), np.float32)
+        w2_s = np.empty((E, b(H), b(I)), np.float32)
+
+    def one(e):
+        g = [np.random.Generator(np.random.PCG64(kids[i][e])) for i in range(4)]
+        if fmt == FMT_MXFP4:
+            w13_q[e] = g[0].integers(0, 256, size=w13_q.shape[1:], dtype=np.uint8)
+            w13_s[e] = g[1].integers(118, 125, size=w13_s.shape[1:], dtype=np.uint8)
+            w2_q[e] = g[2].integers(0, 256, size=w2_q.shape[1:], dtype=np.uint8)
+            w2_s[e] = g[3].integers(118, 125, size=w2_s.shape[1:], dtype=np.uint8)
+        else:
+            w13_q[e] = _fp8_codes(g[0], w13_q.shape[1:])
+            w13_s[e] = (np.abs(g[1].standard_normal(w13_s.shape[1:])) * 3e-4 + 1e-5).astype(np.float32)
+            w2_q[e] = _fp8_codes(g[2], w2_q.shape[1:])
+            w2_s[e] = (np.abs(g[3].standard_normal(w2_s.shape[1:])) * 3e-4 + 1e-5).astype(np.float32)
+
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        list(ex.map(one, range(E)))
+    sh13 = sh2 = None
+    if shape.has_shared:
+        sh13 = bf16_bits(np.random.Generator(np.random.PCG64(d["sh_w13"])).standard_normal((2 * I, H)) * 0.02)
+        sh2 = bf16_bits(np.random.Generator(np.random.PCG64(d["sh_w2"])).standard_normal((H, I)) * 0.02)
+    return FmtLayer(shape, seed, fmt, router, w13_q, w13_s, w2_q, w2_s, sh13, sh2)
+
+
+# Vocabulary of the LM head (bpdata.com article, model section: the LM head
+# projects the 2,560-wide hidden state onto 157,184 tokens).
+LM_VOCAB = 157184
+
+
+def make_lmhead(V: int, H: int, seed: int, threads: int = 8) -> np.ndarray:
+    """A BF16 LM head [V][H]: bf16(N(0,1) * 0.02), drawn in blocks of 4096
+    rows, block b from SeedSequence([seed, 7, b])."""
+    out = np.empty((V, H), np.uint16)
+    starts = list(range(0, V, 4096))
+
+    def one(r0):
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 7, r0 // 4096])))
+        r1 = min(V, r0 + 4096)
+        out[r0:r1] = bf16_bits(rng.standard_normal((r1 - r0, H), dtype=np.float32) * np.float32(0.02))
+
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        list(ex.map(one, starts))
+    return out
