@@ -19,7 +19,8 @@ time beside it.
 
 The same run also measures, each with its own roofline (key "extra"): the
 speculative-verify steps (M = 2 and 4 tokens), one token through 40 stacked
-layers with RMSNorm between them, and one 4096-token prefill chunk; the HBM
+layers with RMSNorm between them, one 4096-token prefill chunk, and the LM
+head for one token as FP8 and as BF16 (157,184 x 2,560); the HBM
 read rate a plain streaming kernel reaches on this part (the achievable
 ceiling); and the CPU oracle on this host's cores and on one core.
 
@@ -56,10 +57,13 @@ STACK_LAYERS = 40
 
 WORKLOAD_NAMES = {"decode": "ling_moe_layer_decode_m1", "verify2": "ling_moe_layer_verify_m2",
                   "verify4": "ling_moe_layer_verify_m4", "stack": "ling_moe_stack40_decode_m1",
-                  "prefill": "ling_moe_layer_prefill_m4096"}
-TOKENS = {"decode": 1, "verify2": 2, "verify4": 4, "stack": 1, "prefill": 4096}
+                  "prefill": "ling_moe_layer_prefill_m4096",
+                  "lmhead_fp8": "ling_lm_head_fp8_m1", "lmhead_bf16": "ling_lm_head_bf16_m1"}
+TOKENS = {"decode": 1, "verify2": 2, "verify4": 4, "stack": 1, "prefill": 4096, "lmhead_fp8": 1, "lmhead_bf16": 1}
 # (timed steps, warm-up steps) of the extra workloads measured beside the headline
-EXTRA_STEPS = {"verify2": (256, 32), "verify4": (256, 32), "stack": (16, 4), "prefill": (8, 2)}
+EXTRA_STEPS = {"verify2": (256, 32), "verify4": (256, 32), "stack": (16, 4), "prefill": (8, 2),
+               "lmhead_fp8": (256, 16), "lmhead_bf16": (128, 8)}
+LM_HIDDEN = 2560
 
 
 def step_bytes(n_unique_experts: int, M: int) -> int:
@@ -339,6 +343,55 @@ def measure_prefill(ctx, K, W):
                          "traffic": measured_traffic(WORKLOAD_NAMES["prefill"]), "flops_per_launch": flops}}
 
 
+def measure_lmhead(ctx, K, W, fp8):
+    """The LM head for one token (M = 1): the BF16 head 157,184 x 2,560, or
+    its FP8 copy (quantised once on the device, outside the timed region);
+    K products replayed from graphs of 32."""
+    torch, B, synth = ctx.torch, ctx.B, ctx.synth
+    V, H = synth.LM_VOCAB, LM_HIDDEN
+    if getattr(ctx, "lm", None) is None:
+        t0 = time.time()
+        wb = torch.from_numpy(synth.make_lmhead(V, H, 1, threads=16).view(np.int16)).cuda()
+        q = torch.empty((V, H), dtype=torch.uint8, device="cuda")
+        sc = torch.empty(V, dtype=torch.float32, device="cuda")
+        B.lmhead_quantize_fp8(wb, q, sc)
+        torch.cuda.synchronize()
+        ctx.lm = (wb, q, sc)
+        log(f"LM head generated and quantised in {time.time() - t0:.1f}s")
+    wb, q, sc = ctx.lm
+    x = torch.from_numpy(synth.make_tokens(ctx.shape, 3, 1).view(np.int16)).cuda()
+    out = torch.empty((1, V), dtype=torch.float32, device="cuda")
+
+    def call():
+        if fp8:
+            B.lmhead_fp8(q, sc, x, out)
+        else:
+            B.lmhead_bf16(wb, x, out)
+
+    for _ in range(W):
+        call()
+    torch.cuda.synchronize()
+    G = 32
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(G):
+            call()
+    reps = max(1, K // G)
+    ms, runs = time_graph_region(ctx, [(g, reps)], ctx.args.runs)
+    ms_per_step = ms / (reps * G)
+    nbytes = V * H * (1 if fp8 else 2) + (V * 4 if fp8 else 0) + H * 2 + V * 4
+    gbs = nbytes / (ms_per_step * 1e-3) / 1e9
+    name = "lmhead_fp8" if fp8 else "lmhead_bf16"
+    log(f"{name}: {reps * G} products, {ms_per_step * 1e3:.2f} us each, {gbs:.0f} GB/s")
+    return {"workload": WORKLOAD_NAMES[name], "tokens_per_step": 1, "steps": reps * G, "warmup": W,
+            "ms_per_step": ms_per_step, "run_ms": [round(r, 4) for r in runs], "gbs": gbs,
+            "us_per_token": ms_per_step * 1e3, "bytes_per_step": float(nbytes),
+            "roofline": {"bound": "hbm", "kernel": f"k_lmhead_gemv<{'fp8' if fp8 else 'bf16'}> ({V} x {H})",
+                         "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "bytes_per_launch": nbytes,
+                         "us_per_launch": round(ms_per_step * 1e3, 3)}}
+
+
 def read_ceiling(ctx, gib=2, runs=5):
     """GB/s of the plain streaming read (moe_probe_read) over a buffer far
     larger than the last-level cache: median of `runs`."""
@@ -390,8 +443,9 @@ def main(argv=None):
     B.lib()
 
     head = args.workload
-    extras = [] if (args.no_extras or head != "decode") else ["verify2", "verify4", "stack", "prefill"]
-    need = 1 if head == "prefill" else args.copies
+    extras = [] if (args.no_extras or head != "decode") else ["verify2", "verify4", "stack", "prefill",
+                                                                "lmhead_fp8", "lmhead_bf16"]
+    need = 1 if head in ("prefill", "lmhead_fp8", "lmhead_bf16") else args.copies
     if head == "stack" or "stack" in extras:
         need = max(need, STACK_LAYERS)
     ctx = Ctx(args, need)
@@ -401,6 +455,9 @@ def main(argv=None):
         K, W = (args.steps, args.warmup) if wl == head else EXTRA_STEPS[wl]
         if wl == "prefill":
             results[wl] = measure_prefill(ctx, K, W)
+            continue
+        if wl in ("lmhead_fp8", "lmhead_bf16"):
+            results[wl] = measure_lmhead(ctx, K, W, wl == "lmhead_fp8")
             continue
         r = measure_steps(ctx, wl, K, W, args.path)
         if TOKENS[wl] > 1 or args.path == "calls" or wl == head:

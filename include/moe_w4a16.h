@@ -243,6 +243,33 @@ int moe_permute(const moe_config* cfg /* host */, const int32_t* topk_ids, int32
  * Returns MOE_OK, or MOE_ERR_DEVICE when the word was non-zero. */
 int moe_get_device_error(void* ws, void* stream, int32_t* code_host /* host */);
 
+/* ---- LM head as FP8 (the step after the last MoE layer) -------------------
+ * bpdata.com Ling-3.0-flash MoE article, "Optimalizáció 2": the BF16 LM head
+ * (model section: hidden 2,560 onto 157,184 tokens) is converted to FP8 when
+ * the head is assembled, which roughly halves the bytes it reads per token.
+ * The pages fix neither the FP8 flavour nor the scale; this library uses E4M3
+ * (the OCP 8-bit float: bias 7, largest finite 448, no infinities) with one
+ * float32 scale per row.
+ *
+ * moe_lmhead_quantize_fp8: one-time.  w [V][H] bf16 -> q [V][H] E4M3 codes
+ *   and scale [V] fp32: scale[v] = amax_v / 448 (1 for an all-zero row) and
+ *   q[v][h] = the E4M3 code nearest to w[v][h] / scale[v] (ties to the even
+ *   code, saturating at +-448), both divisions in float32.
+ * moe_lmhead_fp8: logits [M][V] fp32 = scale[v] * sum_h e4m3(q[v][h]) * x[t][h]
+ *   for x [M][H] bf16, accumulated in fp32.
+ * moe_lmhead_bf16: logits [M][V] fp32 = sum_h w[v][h] * x[t][h] with the BF16
+ *   head itself (the unquantised product, for comparison).
+ * Device pointers owned by the caller; w, q and x 16-byte aligned, scale and
+ * logits 4 (MOE_ERR_ALIGN).  H a positive multiple of 16 and V >= 0
+ * (MOE_ERR_SHAPE; q must not overlap w); the products take M <= 4 and
+ * H = 2560 or H <= 512 (FP8) / 256 (BF16), else MOE_ERR_UNSUPPORTED.  V = 0 or
+ * M = 0 is a no-op.  Asynchronous on `stream`, no allocation. */
+int moe_lmhead_quantize_fp8(const uint16_t* w, int32_t V, int32_t H, uint8_t* q, float* scale, void* stream);
+int moe_lmhead_fp8(const uint8_t* q, const float* scale, int32_t V, int32_t H, const uint16_t* x, int32_t M,
+                   float* logits, void* stream);
+int moe_lmhead_bf16(const uint16_t* w, int32_t V, int32_t H, const uint16_t* x, int32_t M, float* logits,
+                    void* stream);
+
 const char* moe_status_string(int status);
 
 /* Measurement aid, not part of the layer: reads `bytes` of device memory at

@@ -31,7 +31,7 @@ STATUS_NAMES = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_E
 EXPORTS = ("moe_packed_size", "moe_pack_weights", "moe_workspace_size", "moe_workspace_init",
            "moe_route", "moe_forward_w4a16", "moe_layer_w4a16", "moe_gate_up_w4a16", "moe_down_w4a16", "moe_permute",
            "moe_get_device_error", "moe_status_string", "moe_build_info", "moe_probe_read",
-           "moe_layer_w4a16_noalloc")
+           "moe_layer_w4a16_noalloc", "moe_lmhead_quantize_fp8", "moe_lmhead_fp8", "moe_lmhead_bf16")
 
 
 class MoeError(RuntimeError):
@@ -79,6 +79,9 @@ def lib() -> ctypes.CDLL:
                                           ctypes.c_size_t, _P]
             L.moe_layer_w4a16_noalloc.argtypes = [cfgp, _P, _P, _P, ctypes.c_int32, ctypes.c_uint32, _P, _P, _P,
                                                   _P, _P]
+            L.moe_lmhead_quantize_fp8.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
+            L.moe_lmhead_fp8.argtypes = [_P, _P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P, _P]
+            L.moe_lmhead_bf16.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P, _P]
             L.moe_gate_up_w4a16.argtypes = [cfgp, _P, _P, ctypes.c_int32, _P, _P, ctypes.c_size_t, _P]
             L.moe_down_w4a16.argtypes = [cfgp, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t, _P]
             L.moe_permute.argtypes = [cfgp, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t, _P]
@@ -237,3 +240,22 @@ class Workspace:
             raise MoeError("moe_workspace_size", -2, "invalid config or max_tokens")
         self.buf = torch.empty(n, dtype=torch.uint8, device=device)
         workspace_init(self.buf)
+
+
+def lmhead_quantize_fp8(w, q, scale, stream=None):
+    """w bf16 [V][H] -> q uint8 [V][H] (E4M3 codes), scale float32 [V]."""
+    V, H = w.shape
+    _check("moe_lmhead_quantize_fp8", lib().moe_lmhead_quantize_fp8(_ptr(w), V, H, _ptr(q), _ptr(scale), _stream(stream)))
+
+
+def lmhead_fp8(q, scale, x, logits, stream=None):
+    """logits float32 [M][V] from the FP8 head q [V][H], scale [V] and x bf16 [M][H]."""
+    V, H = q.shape
+    _check("moe_lmhead_fp8", lib().moe_lmhead_fp8(_ptr(q), _ptr(scale), V, H, _ptr(x), x.shape[0], _ptr(logits),
+                                                  _stream(stream)))
+
+
+def lmhead_bf16(w, x, logits, stream=None):
+    """logits float32 [M][V] from the BF16 head w [V][H] and x bf16 [M][H]."""
+    V, H = w.shape
+    _check("moe_lmhead_bf16", lib().moe_lmhead_bf16(_ptr(w), V, H, _ptr(x), x.shape[0], _ptr(logits), _stream(stream)))

@@ -282,6 +282,38 @@ int moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t M, int32
                                  reinterpret_cast<int32_t*>(w8 + L.err), static_cast<hipStream_t>(stream)));
 }
 
+int moe_lmhead_quantize_fp8(const uint16_t* w, int32_t V, int32_t H, uint8_t* q, float* scale, void* stream) {
+  if (V < 0 || H <= 0 || H % 16) return MOE_ERR_SHAPE;
+  if (V == 0) return MOE_OK;
+  if (!w || !q || !scale) return MOE_ERR_NULL;
+  if (!aligned16(w) || !aligned16(q) || !aligned4(scale)) return MOE_ERR_ALIGN;
+  if (overlap(w, q, (size_t)V * H)) return MOE_ERR_SHAPE;
+  return launched(launch_lmhead_quant(w, V, H, q, scale, static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+int lmhead_call(bool fp8, const void* w, const float* scale, int32_t V, int32_t H, const uint16_t* x, int32_t M,
+                float* logits, void* stream) {
+  if (V < 0 || H <= 0 || H % 16 || M < 0) return MOE_ERR_SHAPE;
+  if (V == 0 || M == 0) return MOE_OK;
+  if (!w || !x || !logits || (fp8 && !scale)) return MOE_ERR_NULL;
+  if (!aligned16(w) || !aligned16(x) || !aligned4(logits) || (fp8 && !aligned4(scale))) return MOE_ERR_ALIGN;
+  if (M > 4 || !lmhead_supported(H, fp8)) return MOE_ERR_UNSUPPORTED;
+  return launched(launch_lmhead_gemv(fp8, static_cast<const uint8_t*>(w), scale, V, H, x, M, logits,
+                                     static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+int moe_lmhead_fp8(const uint8_t* q, const float* scale, int32_t V, int32_t H, const uint16_t* x, int32_t M,
+                   float* logits, void* stream) {
+  return lmhead_call(true, q, scale, V, H, x, M, logits, stream);
+}
+
+int moe_lmhead_bf16(const uint16_t* w, int32_t V, int32_t H, const uint16_t* x, int32_t M, float* logits,
+                    void* stream) {
+  return lmhead_call(false, w, nullptr, V, H, x, M, logits, stream);
+}
+
 int moe_get_device_error(void* ws, void* stream, int32_t* code_host) {
   if (!ws || !code_host) return MOE_ERR_NULL;
   hipStream_t st = static_cast<hipStream_t>(stream);

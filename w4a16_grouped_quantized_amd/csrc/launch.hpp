@@ -69,4 +69,11 @@ hipError_t launch_pack(const Shape& s, const uint8_t* w13_q, const uint16_t* w13
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 
+// FP8 LM head: per-row E4M3 quantisation of a BF16 head, and the GEMV with an
+// FP8 or the BF16 head (M <= 4 tokens).
+bool lmhead_supported(int H, bool fp8);
+hipError_t launch_lmhead_quant(const uint16_t* w, int V, int H, uint8_t* q, float* s, hipStream_t st);
+hipError_t launch_lmhead_gemv(bool fp8, const uint8_t* w, const float* s, int V, int H, const uint16_t* x, int M,
+                              float* out, hipStream_t st);
+
 }  // namespace moe
