@@ -19,8 +19,9 @@ time beside it.
 
 The same run also measures, each with its own roofline (key "extra"): the
 speculative-verify steps (M = 2 and 4 tokens), one token through 40 stacked
-layers with RMSNorm between them, one 4096-token prefill chunk, and the LM
-head for one token as FP8 and as BF16 (157,184 x 2,560); the HBM
+layers with RMSNorm between them, one 4096-token prefill chunk, the LM head
+for one token as FP8 and as BF16 (157,184 x 2,560), and the decode step with
+the routed experts in MXFP4 and in block FP8; the HBM
 read rate a plain streaming kernel reaches on this part (the achievable
 ceiling); and the CPU oracle on this host's cores and on one core.
 
@@ -58,11 +59,18 @@ STACK_LAYERS = 40
 WORKLOAD_NAMES = {"decode": "ling_moe_layer_decode_m1", "verify2": "ling_moe_layer_verify_m2",
                   "verify4": "ling_moe_layer_verify_m4", "stack": "ling_moe_stack40_decode_m1",
                   "prefill": "ling_moe_layer_prefill_m4096",
-                  "lmhead_fp8": "ling_lm_head_fp8_m1", "lmhead_bf16": "ling_lm_head_bf16_m1"}
-TOKENS = {"decode": 1, "verify2": 2, "verify4": 4, "stack": 1, "prefill": 4096, "lmhead_fp8": 1, "lmhead_bf16": 1}
+                  "lmhead_fp8": "ling_lm_head_fp8_m1", "lmhead_bf16": "ling_lm_head_bf16_m1",
+                  "decode_mxfp4": "ling_moe_layer_mxfp4_decode_m1", "decode_fp8block": "ling_moe_layer_fp8block_decode_m1"}
+TOKENS = {"decode": 1, "verify2": 2, "verify4": 4, "stack": 1, "prefill": 4096, "lmhead_fp8": 1, "lmhead_bf16": 1,
+          "decode_mxfp4": 1, "decode_fp8block": 1}
 # (timed steps, warm-up steps) of the extra workloads measured beside the headline
 EXTRA_STEPS = {"verify2": (256, 32), "verify4": (256, 32), "stack": (16, 4), "prefill": (8, 2),
-               "lmhead_fp8": (256, 16), "lmhead_bf16": (128, 8)}
+               "lmhead_fp8": (256, 16), "lmhead_bf16": (128, 8), "decode_mxfp4": (512, 64),
+               "decode_fp8block": (512, 64)}
+# bytes of one routed expert in the other formats: codes + scales of gate_up and down
+EXPERT_BYTES_FMT = {"decode_mxfp4": 2 * 768 * (2560 // 2 + 2560 // 32) + 2560 * (768 // 2 + 768 // 32),
+                    "decode_fp8block": 2 * 768 * 2560 + 12 * 20 * 4 + 2560 * 768 + 20 * 6 * 4}
+FMT_COPIES = 8
 LM_HIDDEN = 2560
 
 
@@ -392,6 +400,64 @@ def measure_lmhead(ctx, K, W, fp8):
                          "us_per_launch": round(ms_per_step * 1e3, 3)}}
 
 
+def measure_fmt(ctx, wl, K, W):
+    """Decode (M = 1) with the routed experts in MXFP4 or block FP8: one step
+    is moe_route + moe_forward_fmt (three launches), rotating over
+    FMT_COPIES resident copies of the layer (experts, shared expert and
+    router; copy c has the router of layer seed 1000 + c), replayed from
+    graphs of 64 steps."""
+    torch, B, synth, shape = ctx.torch, ctx.B, ctx.synth, ctx.shape
+    fmt = synth.FMT_MXFP4 if wl == "decode_mxfp4" else synth.FMT_FP8_BLOCK
+    t0 = time.time()
+    base = B.FmtLayerDev(synth.make_layer_fmt(shape, 1, fmt, threads=16))
+    copies = [base]
+    for c in range(1, FMT_COPIES):
+        d = B.FmtLayerDev.__new__(B.FmtLayerDev)
+        d.shape, d.fmt, d.cfg = base.shape, base.fmt, base.cfg
+        for name in ("w13_q", "w13_s", "w2_q", "w2_s", "sh_w13", "sh_w2"):
+            setattr(d, name, getattr(base, name).clone())
+        d.weights = B.MoeWeightsFmt(*(B._ptr(getattr(d, n)) for n in ("w13_q", "w13_s", "w2_q", "w2_s",
+                                                                      "sh_w13", "sh_w2")))
+        copies.append(d)
+    for c, d in enumerate(copies):
+        d.router_w = torch.from_numpy(synth.make_router(shape, 1000 + c)).cuda()
+    torch.cuda.synchronize()
+    log(f"{wl}: {FMT_COPIES} copies resident in {time.time() - t0:.1f}s")
+    ws = ctx.workspace(1)
+    X = torch.from_numpy(synth.make_tokens(shape, 2, 64).view(np.int16)).view(torch.bfloat16).cuda()
+    ids = torch.empty((1, shape.top_k), dtype=torch.int32, device="cuda")
+    w = torch.empty((1, shape.top_k), dtype=torch.float32, device="cuda")
+    out = torch.empty((1, shape.hidden), dtype=torch.bfloat16, device="cuda")
+
+    def step(i):
+        d = copies[i % FMT_COPIES]
+        x = X[i % 64:i % 64 + 1]
+        B.route(d.cfg, d.router_w, x, ids, w, ws.buf)
+        B.forward_fmt(d, x, ids, w, out, ws.buf)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    G = 64
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(G):
+            step(i)
+    reps = max(1, K // G)
+    ms, runs = time_graph_region(ctx, [(g, reps)], ctx.args.runs)
+    ms_per_step = ms / (reps * G)
+    nbytes = 8 * EXPERT_BYTES_FMT[wl] + SHARED_GU_BYTES + SHARED_DN_BYTES + ROUTER_BYTES + TOKEN_IO_BYTES
+    gbs = nbytes / (ms_per_step * 1e-3) / 1e9
+    log(f"{wl}: {reps * G} steps, {ms_per_step * 1e3:.2f} us/step, {gbs:.0f} GB/s")
+    return {"workload": WORKLOAD_NAMES[wl], "tokens_per_step": 1, "steps": reps * G, "warmup": W,
+            "ms_per_step": ms_per_step, "run_ms": [round(r, 4) for r in runs], "gbs": gbs,
+            "us_per_token": ms_per_step * 1e3, "bytes_per_step": float(nbytes), "resident_layer_copies": FMT_COPIES,
+            "roofline": {"bound": "hbm", "kernel": "moe_route + moe_forward_fmt (k_route, k_fmt_gate_up, k_fmt_down)",
+                         "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "bytes_per_launch": nbytes,
+                         "us_per_launch": round(ms_per_step * 1e3, 3)}}
+
+
 def read_ceiling(ctx, gib=2, runs=5):
     """GB/s of the plain streaming read (moe_probe_read) over a buffer far
     larger than the last-level cache: median of `runs`."""
@@ -444,8 +510,9 @@ def main(argv=None):
 
     head = args.workload
     extras = [] if (args.no_extras or head != "decode") else ["verify2", "verify4", "stack", "prefill",
-                                                                "lmhead_fp8", "lmhead_bf16"]
-    need = 1 if head in ("prefill", "lmhead_fp8", "lmhead_bf16") else args.copies
+                                                                "lmhead_fp8", "lmhead_bf16", "decode_mxfp4",
+                                                                "decode_fp8block"]
+    need = 1 if head in ("prefill", "lmhead_fp8", "lmhead_bf16", "decode_mxfp4", "decode_fp8block") else args.copies
     if head == "stack" or "stack" in extras:
         need = max(need, STACK_LAYERS)
     ctx = Ctx(args, need)
@@ -458,6 +525,9 @@ def main(argv=None):
             continue
         if wl in ("lmhead_fp8", "lmhead_bf16"):
             results[wl] = measure_lmhead(ctx, K, W, wl == "lmhead_fp8")
+            continue
+        if wl in ("decode_mxfp4", "decode_fp8block"):
+            results[wl] = measure_fmt(ctx, wl, K, W)
             continue
         r = measure_steps(ctx, wl, K, W, args.path)
         if TOKENS[wl] > 1 or args.path == "calls" or wl == head:

@@ -243,6 +243,47 @@ int moe_permute(const moe_config* cfg /* host */, const int32_t* topk_ids, int32
  * Returns MOE_OK, or MOE_ERR_DEVICE when the word was non-zero. */
 int moe_get_device_error(void* ws, void* stream, int32_t* code_host /* host */);
 
+/* ---- routed experts in the other two formats the pages serve ---------------
+ * MXFP4: bpdata.com Ling-3.0-flash MoE article, model section and
+ *   "Optimalizáció 1" (the FP4 checkpoint served with MXFP4 MoE kernels): E2M1
+ *   codes (the OCP 4-bit float: magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) with
+ *   one E8M0 scale 2^(c-127) per 32 consecutive inputs.
+ *     w13_q [E][2I][H/2], w2_q [E][H][I/2]: two codes per byte, the low nibble
+ *     the even input; w13_s [E][2I][H/32], w2_s [E][H][I/32]: uint8 E8M0.
+ * FP8_BLOCK: vLLM recipe page "inclusionAI/Ling-3.0-flash", Overview and
+ *   Prerequisites (the serialized block-FP8 checkpoint, BF16 compute); the
+ *   block shape is this library's reading: E4M3 codes (bias 7, largest 448)
+ *   with one float32 scale per 128 x 128 block.
+ *     w13_q [E][2I][H], w2_q [E][H][I]: one code per byte; w13_s
+ *     [E][ceil(2I/128)][ceil(H/128)], w2_s [E][ceil(H/128)][ceil(I/128)] fp32.
+ * Gate rows [0, I), up rows [I, 2I) as in moe_weights_plain; the shared expert
+ * stays BF16 (sh_w13 [2I][H], sh_w2 [H][I], NULL iff has_shared == 0).  All
+ * row-major, device memory owned by the caller. */
+#define MOE_FMT_MXFP4 1
+#define MOE_FMT_FP8_BLOCK 2
+typedef struct {
+  const uint8_t* w13_q;
+  const void* w13_s;
+  const uint8_t* w2_q;
+  const void* w2_s;
+  const uint16_t* sh_w13;
+  const uint16_t* sh_w2;
+} moe_weights_fmt;
+
+/* moe_forward_w4a16 with the routed experts in format fmt (weights in the
+ * layout above, read as they are: no packing step): out [M][H] bf16 =
+ * sum_j w[t][j] * expert_{ids[t][j]}(x[t]) + shared(x[t]), h = silu(W1 x) *
+ * (W3 x), fp32 accumulation, slots added in order.  Two launches (gate_up,
+ * then down + combine) that allocate nothing.  M <= 8 and M*top_k <= 64
+ * (MOE_ERR_UNSUPPORTED beyond, or for a shape the kernels do not cover);
+ * codes and x, out, the shared weights and ws 16-byte aligned, ids and
+ * weights 4, FP8 scales 4 (MOE_ERR_ALIGN); ws as for moe_forward_w4a16 with
+ * M tokens.  Ids out of range are recorded in the device error word and add
+ * nothing.  M = 0 is a no-op. */
+int moe_forward_fmt(const moe_config* cfg /* host */, int32_t fmt, const moe_weights_fmt* w /* host struct */,
+                    const uint16_t* x, int32_t M, const int32_t* topk_ids, const float* topk_w, uint16_t* out,
+                    void* ws, size_t ws_bytes, void* stream);
+
 /* ---- LM head as FP8 (the step after the last MoE layer) -------------------
  * bpdata.com Ling-3.0-flash MoE article, "Optimalizáció 2": the BF16 LM head
  * (model section: hidden 2,560 onto 157,184 tokens) is converted to FP8 when

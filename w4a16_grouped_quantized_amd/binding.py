@@ -19,6 +19,8 @@ LIB_PATH = os.path.join(_HERE, "libmoe_w4a16.so")
 MOE_F_INPUT_RMSNORM = 0x1
 MOE_F_ONE_LAUNCH = 0x2
 MOE_ERR_WORKSPACE = -4
+MOE_FMT_MXFP4 = 1
+MOE_FMT_FP8_BLOCK = 2
 # bytes of the static workspace of moe_layer_w4a16_noalloc (MOE_NOALLOC_WS_BYTES)
 MOE_NOALLOC_WS_BYTES = 16 << 20
 
@@ -31,7 +33,8 @@ STATUS_NAMES = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_E
 EXPORTS = ("moe_packed_size", "moe_pack_weights", "moe_workspace_size", "moe_workspace_init",
            "moe_route", "moe_forward_w4a16", "moe_layer_w4a16", "moe_gate_up_w4a16", "moe_down_w4a16", "moe_permute",
            "moe_get_device_error", "moe_status_string", "moe_build_info", "moe_probe_read",
-           "moe_layer_w4a16_noalloc", "moe_lmhead_quantize_fp8", "moe_lmhead_fp8", "moe_lmhead_bf16")
+           "moe_layer_w4a16_noalloc", "moe_lmhead_quantize_fp8", "moe_lmhead_fp8", "moe_lmhead_bf16",
+           "moe_forward_fmt")
 
 
 class MoeError(RuntimeError):
@@ -44,6 +47,12 @@ class MoeConfig(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("group_size", ctypes.c_int32), ("has_shared", ctypes.c_int32)]
+
+
+class MoeWeightsFmt(ctypes.Structure):
+    """moe_weights_fmt: device pointers of routed experts in MXFP4 or block FP8."""
+    _fields_ = [("w13_q", ctypes.c_void_p), ("w13_s", ctypes.c_void_p), ("w2_q", ctypes.c_void_p),
+                ("w2_s", ctypes.c_void_p), ("sh_w13", ctypes.c_void_p), ("sh_w2", ctypes.c_void_p)]
 
 
 _P = ctypes.c_void_p
@@ -79,6 +88,8 @@ def lib() -> ctypes.CDLL:
                                           ctypes.c_size_t, _P]
             L.moe_layer_w4a16_noalloc.argtypes = [cfgp, _P, _P, _P, ctypes.c_int32, ctypes.c_uint32, _P, _P, _P,
                                                   _P, _P]
+            L.moe_forward_fmt.argtypes = [cfgp, ctypes.c_int32, ctypes.POINTER(MoeWeightsFmt), _P, ctypes.c_int32,
+                                          _P, _P, _P, _P, ctypes.c_size_t, _P]
             L.moe_lmhead_quantize_fp8.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
             L.moe_lmhead_fp8.argtypes = [_P, _P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P, _P]
             L.moe_lmhead_bf16.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P, _P]
@@ -259,3 +270,34 @@ def lmhead_bf16(w, x, logits, stream=None):
     """logits float32 [M][V] from the BF16 head w [V][H] and x bf16 [M][H]."""
     V, H = w.shape
     _check("moe_lmhead_bf16", lib().moe_lmhead_bf16(_ptr(w), V, H, _ptr(x), x.shape[0], _ptr(logits), _stream(stream)))
+
+
+
+class FmtLayerDev:
+    """A synth.FmtLayer (MXFP4 or block-FP8 routed experts) resident on the
+    GPU in its plain layout, with its router."""
+
+    def __init__(self, layer, device="cuda"):
+        import torch
+        self.shape, self.fmt = layer.shape, layer.fmt
+        self.cfg = config(layer.shape)
+        dev = torch.device(device)
+
+        def up(a):
+            a = np.ascontiguousarray(a)
+            return torch.from_numpy(a.view(np.uint8).reshape(-1)).to(dev)
+
+        self.router_w = torch.from_numpy(np.ascontiguousarray(layer.router_w)).to(dev)
+        self.w13_q, self.w13_s, self.w2_q, self.w2_s = (up(layer.w13_q), up(layer.w13_s), up(layer.w2_q),
+                                                        up(layer.w2_s))
+        self.sh_w13 = up(layer.sh_w13) if layer.shape.has_shared else None
+        self.sh_w2 = up(layer.sh_w2) if layer.shape.has_shared else None
+        self.weights = MoeWeightsFmt(_ptr(self.w13_q), _ptr(self.w13_s), _ptr(self.w2_q), _ptr(self.w2_s),
+                                     _ptr(self.sh_w13), _ptr(self.sh_w2))
+
+
+def forward_fmt(dl: FmtLayerDev, x, topk_ids, topk_w, out, ws, stream=None):
+    """moe_forward_fmt: out bf16 [M][H] with the routed experts of dl."""
+    _check("moe_forward_fmt", lib().moe_forward_fmt(ctypes.byref(dl.cfg), dl.fmt, ctypes.byref(dl.weights), _ptr(x),
+                                                    x.shape[0], _ptr(topk_ids), _ptr(topk_w), _ptr(out), _ptr(ws),
+                                                    ws.numel() * ws.element_size(), _stream(stream)))

@@ -282,6 +282,32 @@ int moe_permute(const moe_config* cfg, const int32_t* topk_ids, int32_t M, int32
                                  reinterpret_cast<int32_t*>(w8 + L.err), static_cast<hipStream_t>(stream)));
 }
 
+int moe_forward_fmt(const moe_config* cfg, int32_t fmt, const moe_weights_fmt* w, const uint16_t* x, int32_t M,
+                    const int32_t* topk_ids, const float* topk_w, uint16_t* out, void* ws, size_t ws_bytes,
+                    void* stream) {
+  Shape s;
+  int rc = check_cfg(cfg, &s);
+  if (rc != MOE_OK) return rc;
+  if (fmt != MOE_FMT_MXFP4 && fmt != MOE_FMT_FP8_BLOCK) return MOE_ERR_UNSUPPORTED;
+  if (M < 0) return MOE_ERR_SHAPE;
+  if (M == 0) return MOE_OK;
+  if (!w || !x || !topk_ids || !topk_w || !out || !ws || !w->w13_q || !w->w13_s || !w->w2_q || !w->w2_s)
+    return MOE_ERR_NULL;
+  if (s.has_shared ? (!w->sh_w13 || !w->sh_w2) : (w->sh_w13 || w->sh_w2)) return MOE_ERR_NULL;
+  if (!aligned16(w->w13_q) || !aligned16(w->w2_q) || !aligned16(x) || !aligned16(out) || !aligned16(ws) ||
+      !aligned4(topk_ids) || !aligned4(topk_w) ||
+      (fmt == MOE_FMT_FP8_BLOCK && (!aligned4(w->w13_s) || !aligned4(w->w2_s))) ||
+      (s.has_shared && (!aligned16(w->sh_w13) || !aligned16(w->sh_w2))))
+    return MOE_ERR_ALIGN;
+  int ra, rsh, rb;
+  if (!fmt_plan(s, fmt, M, &ra, &rsh, &rb)) return MOE_ERR_UNSUPPORTED;
+  const WsLayout L = ws_layout(s.H, s.E, s.k, s.I, s.has_shared, M);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  return launched(launch_forward_fmt(s, fmt, w->w13_q, w->w13_s, w->w2_q, w->w2_s, w->sh_w13, w->sh_w2, x, M,
+                                     topk_ids, topk_w, out, static_cast<uint8_t*>(ws), L,
+                                     static_cast<hipStream_t>(stream)));
+}
+
 int moe_lmhead_quantize_fp8(const uint16_t* w, int32_t V, int32_t H, uint8_t* q, float* scale, void* stream) {
   if (V < 0 || H <= 0 || H % 16) return MOE_ERR_SHAPE;
   if (V == 0) return MOE_OK;

@@ -76,4 +76,13 @@ hipError_t launch_lmhead_quant(const uint16_t* w, int V, int H, uint8_t* q, floa
 hipError_t launch_lmhead_gemv(bool fp8, const uint8_t* w, const float* s, int V, int H, const uint16_t* x, int M,
                               float* out, hipStream_t st);
 
+// Routed experts in MXFP4 or block FP8 (plain layout), M <= 8: gate_up then
+// down + combine, with the shared expert in BF16.
+constexpr int kFmtMxfp4 = 1, kFmtFp8Block = 2, kFmtBf16 = 3;
+bool fmt_plan(const Shape& s, int fmt, int M, int* ra, int* rsh, int* rb);
+hipError_t launch_forward_fmt(const Shape& s, int fmt, const uint8_t* w13_q, const void* w13_s, const uint8_t* w2_q,
+                              const void* w2_s, const uint16_t* sh_w13, const uint16_t* sh_w2, const uint16_t* x,
+                              int M, const int32_t* ids, const float* w, uint16_t* out, uint8_t* ws,
+                              const WsLayout& L, hipStream_t st);
+
 }  // namespace moe
