@@ -20,8 +20,10 @@ time beside it.
 The same run also measures, each with its own roofline (key "extra"): the
 speculative-verify steps (M = 2 and 4 tokens), one token through 40 stacked
 layers with RMSNorm between them, one 4096-token prefill chunk, the LM head
-for one token as FP8 and as BF16 (157,184 x 2,560), and the decode step with
-the routed experts in MXFP4 and in block FP8; the HBM
+for one token as FP8 and as BF16 (157,184 x 2,560), the decode step with
+the routed experts in MXFP4 and in block FP8, and a speculative-decoding
+round (3 draft steps and a 4-position verify on the 40-layer stack, with the
+verify:decode ratio); the HBM
 read rate a plain streaming kernel reaches on this part (the achievable
 ceiling); and the CPU oracle on this host's cores and on one core.
 
@@ -60,13 +62,17 @@ WORKLOAD_NAMES = {"decode": "ling_moe_layer_decode_m1", "verify2": "ling_moe_lay
                   "verify4": "ling_moe_layer_verify_m4", "stack": "ling_moe_stack40_decode_m1",
                   "prefill": "ling_moe_layer_prefill_m4096",
                   "lmhead_fp8": "ling_lm_head_fp8_m1", "lmhead_bf16": "ling_lm_head_bf16_m1",
-                  "decode_mxfp4": "ling_moe_layer_mxfp4_decode_m1", "decode_fp8block": "ling_moe_layer_fp8block_decode_m1"}
+                  "decode_mxfp4": "ling_moe_layer_mxfp4_decode_m1", "decode_fp8block": "ling_moe_layer_fp8block_decode_m1",
+                  "mtp_round": "ling_moe_stack40_mtp_round_3drafts"}
 TOKENS = {"decode": 1, "verify2": 2, "verify4": 4, "stack": 1, "prefill": 4096, "lmhead_fp8": 1, "lmhead_bf16": 1,
-          "decode_mxfp4": 1, "decode_fp8block": 1}
+          "decode_mxfp4": 1, "decode_fp8block": 1, "mtp_round": 4}
 # (timed steps, warm-up steps) of the extra workloads measured beside the headline
 EXTRA_STEPS = {"verify2": (256, 32), "verify4": (256, 32), "stack": (16, 4), "prefill": (8, 2),
                "lmhead_fp8": (256, 16), "lmhead_bf16": (128, 8), "decode_mxfp4": (512, 64),
-               "decode_fp8block": (512, 64)}
+               "decode_fp8block": (512, 64), "mtp_round": (16, 2)}
+# accept length per round the pages report for 3 draft steps (bpdata.com
+# article, "Optimalizáció 3")
+MTP_ACCEPT = 3.90
 # bytes of one routed expert in the other formats: codes + scales of gate_up and down
 EXPERT_BYTES_FMT = {"decode_mxfp4": 2 * 768 * (2560 // 2 + 2560 // 32) + 2560 * (768 // 2 + 768 // 32),
                     "decode_fp8block": 2 * 768 * 2560 + 12 * 20 * 4 + 2560 * 768 + 20 * 6 * 4}
@@ -458,6 +464,75 @@ def measure_fmt(ctx, wl, K, W):
                          "us_per_launch": round(ms_per_step * 1e3, 3)}}
 
 
+def measure_mtp(ctx, K, W):
+    """The speculative-decoding round on the 40-layer stack (mtp.MtpRound):
+    3 draft steps of a draft layer (M = 1 each) and a 4-position verify
+    through the 40 layers; beside it the verify alone and one decode token
+    through the same 40 layers (M = 1), each replayed from graphs."""
+    torch, B, synth, shape, cfg = ctx.torch, ctx.B, ctx.synth, ctx.shape, ctx.cfg
+    from w4a16_grouped_quantized_amd.mtp import MtpRound
+    stack = [ctx.copies[l] for l in range(STACK_LAYERS)]
+    stack = [(rt, pk) for pk, rt in stack]
+    draft = (ctx.copies[STACK_LAYERS][1], ctx.copies[STACK_LAYERS][0])
+    ws = ctx.workspace(4)
+    r = MtpRound(cfg, stack, draft, ws)
+    X = torch.from_numpy(synth.make_tokens(shape, 5, 1).view(np.int16)).view(torch.bfloat16).cuda()
+    r.rows[0:1].copy_(X)
+    # unique experts per verify layer (for the verify's bytes)
+    uniq = []
+    r.round(record_verify=lambda l, xn, ids, w, out: uniq.append(len(set(ids.cpu().numpy().ravel().tolist()))))
+    for _ in range(W):
+        r.round()
+    torch.cuda.synchronize()
+    # decode: one token through the same layers, RMSNorm between them
+    ids1 = torch.empty((1, shape.top_k), dtype=torch.int32, device="cuda")
+    w1 = torch.empty((1, shape.top_k), dtype=torch.float32, device="cuda")
+    b1 = (torch.empty((1, shape.hidden), dtype=torch.bfloat16, device="cuda"),
+          torch.empty((1, shape.hidden), dtype=torch.bfloat16, device="cuda"))
+    xn1 = torch.empty((1, shape.hidden), dtype=torch.bfloat16, device="cuda")
+    ws1 = ctx.workspace(1)
+
+    def decode():
+        for l, (rt, pk) in enumerate(stack):
+            if l == 0:
+                B.layer(cfg, rt, pk, X, ids1, w1, b1[0], ws1.buf)
+            else:
+                B.layer(cfg, rt, pk, b1[(l - 1) % 2], ids1, w1, b1[l % 2], ws1.buf, flags=B.MOE_F_INPUT_RMSNORM,
+                        x_norm=xn1)
+
+    graphs = {}
+    for name, fn in (("round", r.round), ("verify", r.verify), ("drafts", r.drafts), ("decode", decode)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        graphs[name] = g
+    t = {}
+    runs_round = None
+    for name, g in graphs.items():
+        ms, runs = time_graph_region(ctx, [(g, K)], ctx.args.runs)
+        t[name] = ms / K * 1e3
+        if name == "round":
+            runs_round = runs
+    ratio = t["verify"] / t["decode"]
+    vbytes = sum(step_bytes(u, 4) for u in uniq)
+    gbs = vbytes / (t["verify"] * 1e-6) / 1e9
+    log(f"mtp_round: {t['round']:.1f} us/round (drafts {t['drafts']:.1f}, verify {t['verify']:.1f}); decode through "
+        f"{STACK_LAYERS} layers {t['decode']:.1f} us; verify:decode {ratio:.2f}; unique experts per verify layer "
+        f"{np.mean(uniq):.2f}")
+    return {"workload": WORKLOAD_NAMES["mtp_round"], "tokens_per_step": 4, "steps": K, "warmup": W,
+            "ms_per_step": t["round"] / 1e3, "run_ms": [round(x, 4) for x in runs_round],
+            "gbs": gbs, "us_per_token": t["round"] / MTP_ACCEPT, "bytes_per_step": float(vbytes),
+            "us_per_round": round(t["round"], 3), "us_drafts": round(t["drafts"], 3),
+            "us_verify": round(t["verify"], 3), "us_decode_stack": round(t["decode"], 3),
+            "verify_to_decode": round(ratio, 3), "pages_verify_to_decode": 2.26,
+            "unique_experts_per_verify_layer": round(float(np.mean(uniq)), 2),
+            "tokens_per_s_at_accept": {str(a): round(a / (t["round"] * 1e-6), 1) for a in (1.0, 2.0, 3.0, MTP_ACCEPT, 4.0)},
+            "roofline": {"bound": "hbm", "kernel": "verify step: 40 layers at M = 4 (moe_route + moe_forward_w4a16 "
+                                                   "per layer)", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "bytes_per_launch": vbytes, "us_per_launch": round(t["verify"], 3)}}
+
+
 def read_ceiling(ctx, gib=2, runs=5):
     """GB/s of the plain streaming read (moe_probe_read) over a buffer far
     larger than the last-level cache: median of `runs`."""
@@ -511,10 +586,12 @@ def main(argv=None):
     head = args.workload
     extras = [] if (args.no_extras or head != "decode") else ["verify2", "verify4", "stack", "prefill",
                                                                 "lmhead_fp8", "lmhead_bf16", "decode_mxfp4",
-                                                                "decode_fp8block"]
+                                                                "decode_fp8block", "mtp_round"]
     need = 1 if head in ("prefill", "lmhead_fp8", "lmhead_bf16", "decode_mxfp4", "decode_fp8block") else args.copies
     if head == "stack" or "stack" in extras:
         need = max(need, STACK_LAYERS)
+    if head == "mtp_round" or "mtp_round" in extras:
+        need = max(need, STACK_LAYERS + 1)
     ctx = Ctx(args, need)
 
     results = {}
@@ -528,6 +605,9 @@ def main(argv=None):
             continue
         if wl in ("decode_mxfp4", "decode_fp8block"):
             results[wl] = measure_fmt(ctx, wl, K, W)
+            continue
+        if wl == "mtp_round":
+            results[wl] = measure_mtp(ctx, K, W)
             continue
         r = measure_steps(ctx, wl, K, W, args.path)
         if TOKENS[wl] > 1 or args.path == "calls" or wl == head:
