@@ -539,7 +539,7 @@ def read_ceiling(ctx, gib=2, runs=5):
     torch, B = ctx.torch, ctx.B
     n = gib << 30
     buf = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(3)
-    blocks = 4096
+    blocks = 8 * torch.cuda.get_device_properties(0).multi_processor_count
     sink = torch.zeros(blocks, dtype=torch.int32, device="cuda")
     B.probe_read(buf, sink, blocks)
     torch.cuda.synchronize()
@@ -553,10 +553,10 @@ def read_ceiling(ctx, gib=2, runs=5):
         res.append(n / (e0.elapsed_time(e1) * 1e-3) / 1e9)
     del buf
     gbs = float(np.median(res))
-    log(f"read ceiling: {gbs:.0f} GB/s ({gib} GiB, 16-byte loads, {blocks} workgroups; runs "
+    log(f"read ceiling: {gbs:.0f} GB/s ({gib} GiB, 10 KB tiles per wavefront, {blocks} workgroups; runs "
         f"{', '.join(f'{r:.0f}' for r in res)})")
     return {"gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4), "bytes": n,
-            "kernel": "moe_probe_read (grid-stride 16-byte loads, every byte once)"}
+            "kernel": "moe_probe_read (10 KB tiles per wavefront, double-buffered 16-byte loads, every byte once)"}
 
 
 def summary(r, ceiling):
@@ -668,14 +668,19 @@ def main(argv=None):
     print(json.dumps(line), flush=True)
 
 
+DIGEST_EXCLUDED = ("probe.hip",)
+
+
 def kernel_sources_digest() -> str:
-    """sha256 over the HIP sources; a measured traffic figure is valid only
-    for the sources it was measured on."""
+    """sha256 over the HIP sources of the layer's kernels; a measured traffic
+    figure is valid only for the sources it was measured on.  The read-rate
+    probe (probe.hip) is a measurement aid that no layer kernel includes, so
+    it is left out."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "w4a16_grouped_quantized_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp")):
+        if name.endswith((".hip", ".hpp")) and name not in DIGEST_EXCLUDED:
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()

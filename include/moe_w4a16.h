@@ -314,14 +314,15 @@ int moe_lmhead_bf16(const uint16_t* w, int32_t V, int32_t H, const uint16_t* x, 
 const char* moe_status_string(int status);
 
 /* Measurement aid, not part of the layer: reads `bytes` of device memory at
- * `buf` once (16-byte loads, `blocks` workgroups of 256 threads striding over
- * the buffer) and writes nothing unless the xor of the data equals a fixed
- * value (then one word per workgroup into sink[blocks], device memory).  The
- * pages find decode bound by weight reads (bpdata.com article, intro), so the
- * layer's bandwidth is reported against the rate this plain read reaches on
- * the same part as well as against the nominal peak.  buf 16-byte aligned,
- * bytes a multiple of 16 (MOE_ERR_ALIGN), 1 <= blocks <= 65536
- * (MOE_ERR_SHAPE). */
+ * `buf` once (each wavefront of `blocks` workgroups of 256 threads takes
+ * contiguous 10 KB tiles in turn, 16-byte loads, the next tile requested before
+ * the current one is folded) and writes nothing unless the xor of the data
+ * equals a fixed value (then one word per workgroup into sink[blocks], device
+ * memory).  The pages find decode bound by weight reads (bpdata.com article,
+ * intro), so the kernels' bandwidth is reported against the rate this plain
+ * read reaches on the same part as well as against the nominal peak.  buf
+ * 16-byte aligned, bytes a multiple of 16 (MOE_ERR_ALIGN), 1 <= blocks <=
+ * 65536 (MOE_ERR_SHAPE). */
 int moe_probe_read(const void* buf, size_t bytes, uint32_t* sink /* [blocks] */, int32_t blocks, void* stream);
 
 /* Static description of the compiled library: target arch, kernel variants and the

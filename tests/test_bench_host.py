@@ -58,3 +58,8 @@ def test_sources_digest_covers_every_kernel_source():
     csrc = os.path.join(ROOT, "w4a16_grouped_quantized_amd", "csrc")
     names = [n for n in os.listdir(csrc) if n.endswith((".hip", ".hpp"))]
     assert {"layer.hip", "experts.hip", "prefill.hip", "route_dev.hpp", "common.hpp"} <= set(names)
+    # only the read-rate probe, which no layer kernel includes, is left out
+    assert set(bench.DIGEST_EXCLUDED) == {"probe.hip"}
+    for n in names:
+        if n != "probe.hip":
+            assert '#include "probe' not in open(os.path.join(csrc, n)).read()
