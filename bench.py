@@ -672,18 +672,45 @@ DIGEST_EXCLUDED = ("probe.hip",)
 
 
 def kernel_sources_digest() -> str:
-    """sha256 over the HIP sources of the layer's kernels; a measured traffic
-    figure is valid only for the sources it was measured on.  The read-rate
-    probe (probe.hip) is a measurement aid that no layer kernel includes, so
-    it is left out."""
+    """sha256 over the code of the layer's HIP sources (comments and blank
+    lines stripped, see source_code_only); a measured traffic figure is valid
+    only for the code it was measured on.  The read-rate probe (probe.hip) is
+    a measurement aid that no layer kernel includes, so it is left out."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "w4a16_grouped_quantized_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".hpp")) and name not in DIGEST_EXCLUDED:
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+            with open(os.path.join(csrc, name), encoding="utf-8") as f:
+                h.update(name.encode() + b"\0" + source_code_only(f.read()).encode())
     return h.hexdigest()
+
+
+def source_code_only(text: str) -> str:
+    """C++ source without its comments, trailing blanks and empty lines:
+    string and character literals are kept whole (a // or /* inside one is
+    not a comment)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    lines = ("".join(out)).split("\n")
+    return "\n".join(l.rstrip() for l in lines if l.strip())
 
 
 def measured_traffic(workload: str):

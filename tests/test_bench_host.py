@@ -63,3 +63,12 @@ def test_sources_digest_covers_every_kernel_source():
     for n in names:
         if n != "probe.hip":
             assert '#include "probe' not in open(os.path.join(csrc, n)).read()
+
+
+def test_source_digest_ignores_comments_not_code():
+    src = 'int a = 1; // note\n/* block\n comment */ int b = 2;\n\n  const char* s = "//x/*y*/";  \nchar q = \'"\';\n'
+    got = bench.source_code_only(src)
+    assert got == 'int a = 1;\n  int b = 2;\n  const char* s = "//x/*y*/";\nchar q = \'"\';'
+    assert bench.source_code_only(src.replace("note", "other note")) == got
+    assert bench.source_code_only(src.replace("b = 2", "b = 3")) != got
+

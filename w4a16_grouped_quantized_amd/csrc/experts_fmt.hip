@@ -17,13 +17,15 @@
 //
 // Two launches:
 //   k_fmt_gate_up  one workgroup per (distinct expert, block of rows) of W1/W3
-//                  and per block of the shared expert's rows: every chunk's
-//                  product per token into LDS, then each row summed in chunk
-//                  order into gu[slot][2I] (fp32, workspace);
-//   k_fmt_down     one workgroup per block of output rows: h = silu(gate) * up
-//                  of every slot of a token and of the shared expert (bf16
-//                  hi/lo pairs in LDS), the down rows' chunk products, and per
-//                  row sum_j w_j * (W2_j h_j) + W2_sh h_sh in slot order.
+//                  and per block of the shared expert's rows, each block
+//                  holding matching gate and up rows: every chunk's product
+//                  per token into LDS, each row summed in chunk order, then
+//                  h = silu(gate) * up of the block's rows into the workspace
+//                  as a bf16 (hi, lo) pair per value;
+//   k_fmt_down     one workgroup per block of output rows: the h of every
+//                  slot of a token and of the shared expert staged in LDS,
+//                  the down rows' chunk products, and per row
+//                  sum_j w_j * (W2_j h_j) + W2_sh h_sh in slot order.
 #include <algorithm>
 
 #include "experts_dev.hpp"
