@@ -290,6 +290,33 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// The same sum through the ALU's lane moves instead of the LDS crossbar:
+// lane pairs, quads, 8-lane and 16-lane groups by DPP, the two rows of each
+// half by a swizzle, the two halves by scalar reads; every lane gets the
+// same bits.  A mirror move pairs each lane with a lane of the other group,
+// whose value at that point is that group's sum, so each step adds the same
+// two partial sums as a butterfly would (addition commutes).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_move<0xB1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp_move<0x4E>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp_move<0x141>(v);  // row_half_mirror: the other quad of 8 lanes
+  v += dpp_move<0x140>(v);  // row_mirror: the other 8 lanes of a row
+  v += __uint_as_float((uint32_t)__builtin_amdgcn_ds_swizzle((int)__float_as_uint(v), 0x401F));  // lane ^ 16
+  const float h0 = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 0));
+  const float h1 = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 32));
+  return h0 + h1;
+}
+
+// Two floats to a bf16 pair (round to nearest even), in one instruction.
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));

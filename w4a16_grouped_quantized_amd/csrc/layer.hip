@@ -353,7 +353,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         acc = fmaf(wr[i].z, xv[i][2], acc);
         acc = fmaf(wr[i].w, xv[i][3], acc);
       }
-      acc = wave_sum(acc);
+      acc = wave_sum_dpp(acc);
       if (lane == 0) red[wave][t] = acc;
     }
     const uint32_t T = share_tag(ev, &tag_lds);

@@ -317,25 +317,27 @@ __device__ __forceinline__ void decode_token(int H, bool rmsnorm, float eps, flo
   for (int i = 0; i < NI; ++i)
 #pragma unroll
     for (int q = 0; q < 4; ++q) ss = fmaf(xv[i][q], xv[i][q], ss);
-  ss = wave_sum(ss);
-  const float d = rms_divisor(ss, H, eps);
+  ss = wave_sum_dpp(ss);
+  // x / d as x * (1 / d): within about one fp32 ulp of the quotient, so the
+  // bf16 result is the correctly rounded one or its neighbour
+  const float rd = 1.0f / rms_divisor(ss, H, eps);
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    uint16_t bq[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      bq[q] = f32_to_bf16(xv[i][q] / d);
-      xv[i][q] = bf16_to_f32(bq[q]);
-    }
-    packed[i].x = (uint32_t)bq[0] | ((uint32_t)bq[1] << 16);
-    packed[i].y = (uint32_t)bq[2] | ((uint32_t)bq[3] << 16);
+    const uint32_t lo = f32x2_to_bf16x2(xv[i][0] * rd, xv[i][1] * rd);
+    const uint32_t hi = f32x2_to_bf16x2(xv[i][2] * rd, xv[i][3] * rd);
+    xv[i][0] = __uint_as_float(lo << 16);
+    xv[i][1] = __uint_as_float(lo & 0xFFFF0000u);
+    xv[i][2] = __uint_as_float(hi << 16);
+    xv[i][3] = __uint_as_float(hi & 0xFFFF0000u);
+    packed[i].x = lo;
+    packed[i].y = hi;
   }
 }
 
 // One wavefront's view of token t: lane l holds inputs 256*i + 4*l .. +3 as
 // float (raw, or RMS-normalised and rounded to bf16); `packed` receives the
 // same values as bf16 pairs.  The sum of squares runs in a fixed order
-// (i, then the 4 inputs, then the xor butterfly), so every wavefront that
+// (i, then the 4 inputs, then wave_sum_dpp), so every wavefront that
 // calls this gets the same bits.
 template <int NI>
 __device__ __forceinline__ void load_token(const uint16_t* __restrict__ xt, int H, int lane, bool rmsnorm, float eps,
@@ -384,7 +386,7 @@ __device__ __forceinline__ void router_row(const RouteArgs& a, int e, int lane, 
         acc = fmaf(wr[i].z, xv[i][2], acc);
         acc = fmaf(wr[i].w, xv[i][3], acc);
       }
-      acc = wave_sum(acc);
+      acc = wave_sum_dpp(acc);
       if (has_row && lane == 0) {
         if (keys) {
           const uint32_t key = sort_key(acc);  // 0 only for one NaN pattern: stored as the lowest key instead
