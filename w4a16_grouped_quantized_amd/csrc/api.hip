@@ -371,7 +371,7 @@ const char* moe_status_string(int status) {
 }
 
 const char* moe_build_info(void) {
-  return "arch=gfx950 layout=tile64-lanerow-v2 "
+  return "arch=gfx950 layout=tile64-lanerow-expert-major-v3 "
          "route=wave-per-row-fp32+lastwg-topk|mfma-bf16x3(M>=33) "
          "gate_up=int4-dot2bf16-sgpr-act(GW20P4|GW2P2)+shared-bf16(KS-split,lastwg) "
          "down=int4-dot2bf16(GW6P2|GW1P1)+lastwg-combine "

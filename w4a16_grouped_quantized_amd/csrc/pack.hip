@@ -4,9 +4,10 @@
 
 namespace moe {
 
-// One thread per 16-byte output chunk (tile, group, lane) of one expert.
-__global__ void k_pack_codes(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int E, int N,
-                             int K, int is_gu, int I, size_t stride) {
+// One thread per 16-byte output chunk (tile, group, lane) of one expert;
+// expert e's codes at src + e * sstride (plain) and dst + e * dstride.
+__global__ void k_pack_codes(const uint8_t* __restrict__ src, size_t sstride, uint8_t* __restrict__ dst,
+                             size_t dstride, int E, int N, int K, int is_gu, int I) {
   const int GK = K / kGroup, T = N / 64;
   const size_t per_e = (size_t)T * GK * kWave;
   const size_t total = per_e * E;
@@ -17,7 +18,7 @@ __global__ void k_pack_codes(const uint8_t* __restrict__ src, uint8_t* __restric
     const int g = (int)((r0 / kWave) % GK);
     const int b = (int)(r0 / ((size_t)kWave * GK));
     const int row = is_gu ? gu_row(b, l, I) : 64 * b + l;
-    const uint8_t* s = src + (size_t)e * stride + (size_t)row * (K / 2) + (size_t)g * 16;
+    const uint8_t* s = src + (size_t)e * sstride + (size_t)row * (K / 2) + (size_t)g * 16;
     uint32_t d[4];
 #pragma unroll
     for (int dw = 0; dw < 4; ++dw) {
@@ -30,14 +31,15 @@ __global__ void k_pack_codes(const uint8_t* __restrict__ src, uint8_t* __restric
       }
       d[dw] = v;
     }
-    *reinterpret_cast<uint4*>(dst + (size_t)e * stride + ((size_t)(b * GK + g) * kWave + l) * 16) =
+    *reinterpret_cast<uint4*>(dst + (size_t)e * dstride + ((size_t)(b * GK + g) * kWave + l) * 16) =
         make_uint4(d[0], d[1], d[2], d[3]);
   }
 }
 
-// One thread per (tile, pack of P groups, lane) of one expert.
-__global__ void k_pack_scales(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst, int E, int N,
-                              int K, int is_gu, int I, int P, size_t stride_el) {
+// One thread per (tile, pack of P groups, lane) of one expert; strides in
+// elements, as for k_pack_codes.
+__global__ void k_pack_scales(const uint16_t* __restrict__ src, size_t sstride, uint16_t* __restrict__ dst,
+                              size_t dstride, int E, int N, int K, int is_gu, int I, int P) {
   const int GK = K / kGroup, T = N / 64, NP = GK / P;
   const size_t per_e = (size_t)T * NP * kWave;
   const size_t total = per_e * E;
@@ -48,8 +50,8 @@ __global__ void k_pack_scales(const uint16_t* __restrict__ src, uint16_t* __rest
     const int gp = (int)((r0 / kWave) % NP);
     const int b = (int)(r0 / ((size_t)kWave * NP));
     const int row = is_gu ? gu_row(b, l, I) : 64 * b + l;
-    const uint16_t* s = src + (size_t)e * stride_el + (size_t)row * GK + (size_t)gp * P;
-    uint16_t* d = dst + (size_t)e * stride_el + ((size_t)(b * NP + gp) * kWave + l) * P;
+    const uint16_t* s = src + (size_t)e * sstride + (size_t)row * GK + (size_t)gp * P;
+    uint16_t* d = dst + (size_t)e * dstride + ((size_t)(b * NP + gp) * kWave + l) * P;
     for (int q = 0; q < P; ++q) d[q] = s[q];
   }
 }
@@ -169,20 +171,20 @@ hipError_t launch_pack(const Shape& s, const uint8_t* w13_q, const uint16_t* w13
   const KSplit kg = ksplit_for(H / kGroup), kd = ksplit_for(I / kGroup);
   hipError_t err;
   size_t n = (size_t)E * (2 * I / 64) * (H / kGroup) * kWave;
-  hipLaunchKernelGGL(k_pack_codes, dim3(grid_for(n)), dim3(256), 0, st, w13_q, packed + P.gu_q, E, 2 * I, H, 1, I,
-                     P.gu_q_stride);
+  hipLaunchKernelGGL(k_pack_codes, dim3(grid_for(n)), dim3(256), 0, st, w13_q, gu_codes_bytes(H, I), packed + P.gu_q,
+                     P.gu_q_stride, E, 2 * I, H, 1, I);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   n = (size_t)E * (2 * I / 64) * (H / kGroup / kg.P) * kWave;
-  hipLaunchKernelGGL(k_pack_scales, dim3(grid_for(n)), dim3(256), 0, st, w13_s,
-                     reinterpret_cast<uint16_t*>(packed + P.gu_s), E, 2 * I, H, 1, I, kg.P, P.gu_s_stride / 2);
+  hipLaunchKernelGGL(k_pack_scales, dim3(grid_for(n)), dim3(256), 0, st, w13_s, gu_scales_bytes(H, I) / 2,
+                     reinterpret_cast<uint16_t*>(packed + P.gu_s), P.gu_s_stride / 2, E, 2 * I, H, 1, I, kg.P);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   n = (size_t)E * (H / 64) * (I / kGroup) * kWave;
-  hipLaunchKernelGGL(k_pack_codes, dim3(grid_for(n)), dim3(256), 0, st, w2_q, packed + P.dn_q, E, H, I, 0, I,
-                     P.dn_q_stride);
+  hipLaunchKernelGGL(k_pack_codes, dim3(grid_for(n)), dim3(256), 0, st, w2_q, dn_codes_bytes(H, I), packed + P.dn_q,
+                     P.dn_q_stride, E, H, I, 0, I);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   n = (size_t)E * (H / 64) * (I / kGroup / kd.P) * kWave;
-  hipLaunchKernelGGL(k_pack_scales, dim3(grid_for(n)), dim3(256), 0, st, w2_s,
-                     reinterpret_cast<uint16_t*>(packed + P.dn_s), E, H, I, 0, I, kd.P, P.dn_s_stride / 2);
+  hipLaunchKernelGGL(k_pack_scales, dim3(grid_for(n)), dim3(256), 0, st, w2_s, dn_scales_bytes(H, I) / 2,
+                     reinterpret_cast<uint16_t*>(packed + P.dn_s), P.dn_s_stride / 2, E, H, I, 0, I, kd.P);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   uint32_t* meta = reinterpret_cast<uint32_t*>(packed + P.meta);
   if ((err = launch_fill_zero(meta, (size_t)E * kMetaWords * 4, st)) != hipSuccess) return err;
