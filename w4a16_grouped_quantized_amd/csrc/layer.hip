@@ -484,6 +484,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     if (u >= uexp[kMaxUnits]) return;
     const int e = uexp[u];
     uint64_t m = umask[u];
+    LTRACE(3);
     const bool active = wave * GWG < GK;
     const int g0 = active ? wave * GWG : 0;
     // the scales first, so that each group's product waits for its own
@@ -494,6 +495,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 #pragma unroll
     for (int j = 0; j < GWG / PG; ++j) sc[j].load(sb + (size_t)j * kWave * PG);
     __builtin_amdgcn_sched_barrier(0);
+    LTRACE(4);
     const uint8_t* qb = a.gu_q + (size_t)e * a.gu_q_stride + ((size_t)(b * GK + g0) * kWave + lane) * 16;
 #pragma unroll
     for (int i = 0; i < GWG; ++i) wq[i] = *reinterpret_cast<const uint4*>(qb + (size_t)i * kWave * 16);
