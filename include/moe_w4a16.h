@@ -284,6 +284,33 @@ int moe_forward_fmt(const moe_config* cfg /* host */, int32_t fmt, const moe_wei
                     const uint16_t* x, int32_t M, const int32_t* topk_ids, const float* topk_w, uint16_t* out,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* The MXFP4 layer in one launch, as moe_layer_w4a16 is for INT4: the
+ * routed experts in MXFP4 (the FP4 checkpoint the bpdata.com article's model
+ * section and "Optimalizáció 1" serve with MXFP4 MoE kernels), packed once
+ * by moe_pack_weights_mxfp4 into the library's tiled layout (each 16-byte
+ * row-group as the checkpoint stores it, the E8M0 scale bytes packed like
+ * the INT4 layout's bf16 scales, the shared BF16 expert as for INT4, each
+ * expert's parts contiguous).
+ * moe_packed_size_mxfp4: bytes of that layout (0 on an invalid config).
+ * moe_pack_weights_mxfp4: src holds DEVICE pointers in the moe_weights_fmt
+ *   MXFP4 layout; packed (device, caller-owned, not overlapping the sources)
+ *   of packed_bytes; MOE_ERR_NULL / MOE_ERR_ALIGN (16 bytes for the codes,
+ *   the shared weights and packed) / MOE_ERR_WORKSPACE as moe_pack_weights.
+ * moe_layer_mxfp4: arguments, results and errors as moe_layer_w4a16 (flags:
+ *   MOE_F_INPUT_RMSNORM); ids and weights equal moe_route's bit for bit and
+ *   out agrees with moe_route + moe_forward_fmt on the plain weights within
+ *   their rounding (h kept as scaled fp16).  Only the shapes and token counts
+ *   the one-launch layer covers (M <= 4, M * top_k <= 64, a grid the device
+ *   holds at once): MOE_ERR_UNSUPPORTED otherwise, with nothing launched;
+ *   use moe_route + moe_forward_fmt there. */
+size_t moe_packed_size_mxfp4(const moe_config* cfg /* host */);
+int moe_pack_weights_mxfp4(const moe_config* cfg /* host */, const moe_weights_fmt* src /* host struct */,
+                           void* packed, size_t packed_bytes, void* stream);
+int moe_layer_mxfp4(const moe_config* cfg /* host */, const float* router_w, const void* packed,
+                    const uint16_t* x, int32_t M, uint32_t flags, uint16_t* x_norm,
+                    int32_t* topk_ids, float* topk_w, uint16_t* out,
+                    void* ws, size_t ws_bytes, void* stream);
+
 /* ---- LM head as FP8 (the step after the last MoE layer) -------------------
  * bpdata.com Ling-3.0-flash MoE article, "Optimalizáció 2": the BF16 LM head
  * (model section: hidden 2,560 onto 157,184 tokens) is converted to FP8 when

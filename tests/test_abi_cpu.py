@@ -168,3 +168,36 @@ def test_noalloc_limits_checked_on_the_host(lib):
     assert lib.moe_layer_w4a16_noalloc(ctypes.byref(cfg), a, a, a, -1, *args) == -2
     assert lib.moe_layer_w4a16_noalloc(ctypes.byref(cfg), a, a, a, 0, *args) == 0
     assert lib.moe_layer_w4a16_noalloc(None, a, a, a, 1, *args) == -1
+
+
+def test_mxfp4_layer_host_checks(lib):
+    """The MXFP4 one-launch entry points refuse bad arguments on the host
+    (nothing is launched): the packed size counts one byte per E8M0 scale,
+    and the layer covers only what the one-launch kernel covers."""
+    cfg = B.config(synth.LING)
+    E, H, I = 512, 2560, 768
+    plain = E * (2 * I * H // 2 + 2 * I * (H // 32) + H * I // 2 + H * (I // 32)) + (2 * I * H + H * I) * 2
+    assert lib.moe_packed_size_mxfp4(ctypes.byref(cfg)) == plain + E * 16
+    assert lib.moe_packed_size_mxfp4(ctypes.byref(cfg)) < lib.moe_packed_size(ctypes.byref(cfg))
+    a = ctypes.c_void_p(0x10000)
+    odd = ctypes.c_void_p(0x10001)
+    w = B.MoeWeightsFmt(a, a, a, a, a, a)
+    n = lib.moe_packed_size_mxfp4(ctypes.byref(cfg))
+    assert lib.moe_pack_weights_mxfp4(ctypes.byref(cfg), None, a, n, None) == -1
+    assert lib.moe_pack_weights_mxfp4(ctypes.byref(cfg), ctypes.byref(w), a, n - 1, None) == B.MOE_ERR_WORKSPACE
+    assert lib.moe_pack_weights_mxfp4(ctypes.byref(cfg), ctypes.byref(w), odd, n, None) == -3
+    nos = B.MoeWeightsFmt(a, a, a, a, None, None)
+    assert lib.moe_pack_weights_mxfp4(ctypes.byref(cfg), ctypes.byref(nos), a, n, None) == -1
+    ws = 1 << 30
+
+    def call(M, flags=0, x=a, x_norm=None, out=a):
+        return lib.moe_layer_mxfp4(ctypes.byref(cfg), a, a, x, M, flags, x_norm, a, a, out, a, ws, None)
+
+    assert call(0) == 0
+    assert call(-1) == -2
+    assert call(1, flags=B.MOE_F_ONE_LAUNCH) == -2  # only MOE_F_INPUT_RMSNORM
+    assert call(1, flags=B.MOE_F_INPUT_RMSNORM) == -1  # x_norm missing
+    assert call(1, flags=B.MOE_F_INPUT_RMSNORM, x_norm=a) == -2  # x_norm overlaps x
+    assert call(1, out=odd) == -3
+    assert call(5) == -5  # more tokens than the one launch takes
+    assert lib.moe_layer_mxfp4(None, a, a, a, 1, 0, None, a, a, a, a, ws, None) == -1

@@ -34,7 +34,7 @@ EXPORTS = ("moe_packed_size", "moe_pack_weights", "moe_workspace_size", "moe_wor
            "moe_route", "moe_forward_w4a16", "moe_layer_w4a16", "moe_gate_up_w4a16", "moe_down_w4a16", "moe_permute",
            "moe_get_device_error", "moe_status_string", "moe_build_info", "moe_probe_read",
            "moe_layer_w4a16_noalloc", "moe_lmhead_quantize_fp8", "moe_lmhead_fp8", "moe_lmhead_bf16",
-           "moe_forward_fmt")
+           "moe_forward_fmt", "moe_packed_size_mxfp4", "moe_pack_weights_mxfp4", "moe_layer_mxfp4")
 
 
 class MoeError(RuntimeError):
@@ -90,6 +90,11 @@ def lib() -> ctypes.CDLL:
                                                   _P, _P]
             L.moe_forward_fmt.argtypes = [cfgp, ctypes.c_int32, ctypes.POINTER(MoeWeightsFmt), _P, ctypes.c_int32,
                                           _P, _P, _P, _P, ctypes.c_size_t, _P]
+            L.moe_packed_size_mxfp4.restype = ctypes.c_size_t
+            L.moe_packed_size_mxfp4.argtypes = [cfgp]
+            L.moe_pack_weights_mxfp4.argtypes = [cfgp, ctypes.POINTER(MoeWeightsFmt), _P, ctypes.c_size_t, _P]
+            L.moe_layer_mxfp4.argtypes = [cfgp, _P, _P, _P, ctypes.c_int32, ctypes.c_uint32, _P, _P, _P, _P, _P,
+                                          ctypes.c_size_t, _P]
             L.moe_lmhead_quantize_fp8.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
             L.moe_lmhead_fp8.argtypes = [_P, _P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P, _P]
             L.moe_lmhead_bf16.argtypes = [_P, ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P, _P]
@@ -294,6 +299,36 @@ class FmtLayerDev:
         self.sh_w2 = up(layer.sh_w2) if layer.shape.has_shared else None
         self.weights = MoeWeightsFmt(_ptr(self.w13_q), _ptr(self.w13_s), _ptr(self.w2_q), _ptr(self.w2_s),
                                      _ptr(self.sh_w13), _ptr(self.sh_w2))
+
+
+class MxLayerDev:
+    """An MXFP4 synth.FmtLayer packed into the tiled layout of the one-launch
+    layer (moe_pack_weights_mxfp4), with its router; the plain device copy is
+    released after packing unless keep_plain."""
+
+    def __init__(self, layer, device="cuda", keep_plain: bool = False):
+        import torch
+        if layer.fmt != MOE_FMT_MXFP4:
+            raise ValueError("MxLayerDev takes an MXFP4 layer")
+        plain = FmtLayerDev(layer, device)
+        self.shape, self.cfg, self.router_w = plain.shape, plain.cfg, plain.router_w
+        n = lib().moe_packed_size_mxfp4(ctypes.byref(self.cfg))
+        if n == 0:
+            raise MoeError("moe_packed_size_mxfp4", -2, "invalid config")
+        self.packed = torch.empty(n, dtype=torch.uint8, device=device)
+        _check("moe_pack_weights_mxfp4",
+               lib().moe_pack_weights_mxfp4(ctypes.byref(self.cfg), ctypes.byref(plain.weights), _ptr(self.packed),
+                                            n, _stream(None)))
+        torch.cuda.current_stream().synchronize()
+        self.plain = plain if keep_plain else None
+
+
+def layer_mxfp4(cfg, router_w, packed, x, topk_ids, topk_w, out, ws, flags: int = 0, x_norm=None, stream=None):
+    """moe_layer_mxfp4: the MXFP4 layer in one launch (packed by MxLayerDev)."""
+    M = x.shape[0]
+    _check("moe_layer_mxfp4", lib().moe_layer_mxfp4(ctypes.byref(cfg), _ptr(router_w), _ptr(packed), _ptr(x), M,
+                                                    flags, _ptr(x_norm), _ptr(topk_ids), _ptr(topk_w), _ptr(out),
+                                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def forward_fmt(dl: FmtLayerDev, x, topk_ids, topk_w, out, ws, stream=None):

@@ -308,6 +308,56 @@ int moe_forward_fmt(const moe_config* cfg, int32_t fmt, const moe_weights_fmt* w
                                      static_cast<hipStream_t>(stream)));
 }
 
+size_t moe_packed_size_mxfp4(const moe_config* cfg) {
+  Shape s;
+  if (check_cfg(cfg, &s) != MOE_OK) return 0;
+  return packed_layout(s.H, s.E, s.I, s.has_shared, 1).total;
+}
+
+int moe_pack_weights_mxfp4(const moe_config* cfg, const moe_weights_fmt* src, void* packed, size_t packed_bytes,
+                           void* stream) {
+  Shape s;
+  int rc = check_cfg(cfg, &s);
+  if (rc != MOE_OK) return rc;
+  if (!src || !packed || !src->w13_q || !src->w13_s || !src->w2_q || !src->w2_s) return MOE_ERR_NULL;
+  if (s.has_shared ? (!src->sh_w13 || !src->sh_w2) : (src->sh_w13 || src->sh_w2)) return MOE_ERR_NULL;
+  if (!aligned16(packed) || !aligned16(src->w13_q) || !aligned16(src->w2_q) ||
+      (s.has_shared && (!aligned16(src->sh_w13) || !aligned16(src->sh_w2))))
+    return MOE_ERR_ALIGN;
+  const PackedLayout P = packed_layout(s.H, s.E, s.I, s.has_shared, 1);
+  if (packed_bytes < P.total) return MOE_ERR_WORKSPACE;
+  return launched(launch_pack_mxfp4(s, static_cast<const uint8_t*>(src->w13_q), static_cast<const uint8_t*>(src->w13_s),
+                                    static_cast<const uint8_t*>(src->w2_q), static_cast<const uint8_t*>(src->w2_s),
+                                    src->sh_w13, src->sh_w2, static_cast<uint8_t*>(packed), P,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int moe_layer_mxfp4(const moe_config* cfg, const float* router_w, const void* packed, const uint16_t* x, int32_t M,
+                    uint32_t flags, uint16_t* x_norm, int32_t* topk_ids, float* topk_w, uint16_t* out, void* ws,
+                    size_t ws_bytes, void* stream) {
+  Shape s;
+  int rc = check_cfg(cfg, &s);
+  if (rc != MOE_OK) return rc;
+  if (M < 0 || (flags & ~MOE_F_INPUT_RMSNORM)) return MOE_ERR_SHAPE;
+  if (M == 0) return MOE_OK;
+  const bool rms = (flags & MOE_F_INPUT_RMSNORM) != 0;
+  if (!router_w || !packed || !x || !topk_ids || !topk_w || !out || !ws || (rms && !x_norm)) return MOE_ERR_NULL;
+  if (!aligned16(router_w) || !aligned16(packed) || !aligned16(x) || !aligned16(out) || !aligned16(ws) ||
+      !aligned4(topk_ids) || !aligned4(topk_w) || (rms && !aligned16(x_norm)))
+    return MOE_ERR_ALIGN;
+  if (rms && overlap(x, x_norm, (size_t)M * s.H * 2)) return MOE_ERR_SHAPE;
+  if (!layer_supported(s, M) || !route_supported(s)) return MOE_ERR_UNSUPPORTED;
+  WsLayout L;
+  rc = check_experts(cfg, &s, packed, x, M, topk_ids, topk_w, out, ws, ws_bytes, true, true, &L);
+  if (rc != MOE_OK) return rc;
+  const PackedLayout P = packed_layout(s.H, s.E, s.I, s.has_shared, 1);
+  const hipError_t e = launch_layer(s, static_cast<const uint8_t*>(packed), P, router_w, x, M, true, rms, kRmsEps,
+                                    x_norm, topk_ids, topk_w, out, static_cast<uint8_t*>(ws), L,
+                                    static_cast<hipStream_t>(stream), true);
+  // no second path for this layout: a grid the device cannot hold at once is unsupported
+  return e == hipErrorInvalidConfiguration ? MOE_ERR_UNSUPPORTED : launched(e);
+}
+
 int moe_lmhead_quantize_fp8(const uint16_t* w, int32_t V, int32_t H, uint8_t* q, float* scale, void* stream) {
   if (V < 0 || H <= 0 || H % 16) return MOE_ERR_SHAPE;
   if (V == 0) return MOE_OK;

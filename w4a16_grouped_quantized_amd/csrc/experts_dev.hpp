@@ -284,6 +284,76 @@ __device__ __forceinline__ float routed_dot_lds(const uint4 (&wq)[GW], const Sca
   return acc;
 }
 
+// ---- MXFP4 routed experts (tiled layout, codes as the checkpoint stores
+// them, E8M0 scale bytes packed P per lane-load)
+
+// P E8M0 scale bytes of consecutive groups.
+template <int P>
+struct ScaleBytes {
+  uint32_t w;
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ p) {
+    if constexpr (P == 4) w = *reinterpret_cast<const uint32_t*>(p);
+    else if constexpr (P == 2) w = *reinterpret_cast<const uint16_t*>(p);
+    else w = *p;
+  }
+  __device__ __forceinline__ uint32_t get(int q) const { return (w >> (8 * q)) & 0xFFu; }
+};
+
+// v * 2^(c - 127), exact (the E8M0 scale c; c = 255 is NaN).
+__device__ __forceinline__ float e8m0_scaled(float v, uint32_t c, int extra = 0) {
+  return c == 255u ? __builtin_nanf("") : ldexpf(v, (int)c - 127 + extra);
+}
+
+// Byte BYTE of v (two E2M1 codes, the low nibble first) as an exact bf16 or
+// fp16 pair, by the part's scaled converters with scale 1.
+template <int BYTE>
+__device__ __forceinline__ uint32_t fp4x2_bf16(uint32_t v) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((int)v, 1.0f, BYTE));
+}
+template <int BYTE>
+__device__ __forceinline__ uint32_t fp4x2_f16(uint32_t v) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, BYTE));
+}
+
+// One 32-input MXFP4 group (byte b of dword d: inputs 8d+2b, 8d+2b+1)
+// against 16 dwords of bf16 activations in natural pairs, unscaled.
+__device__ __forceinline__ float dot_group_fp4(uint4 w, const uint32_t* xg) {
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+  float p = 0.f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    p = dot2_bf16(fp4x2_bf16<0>(wd[d]), xg[4 * d], p);
+    p = dot2_bf16(fp4x2_bf16<1>(wd[d]), xg[4 * d + 1], p);
+    p = dot2_bf16(fp4x2_bf16<2>(wd[d]), xg[4 * d + 2], p);
+    p = dot2_bf16(fp4x2_bf16<3>(wd[d]), xg[4 * d + 3], p);
+  }
+  return p;
+}
+
+// routed_dot_lds for MXFP4 rows: each group's sum scaled by its E8M0 scale.
+template <int GW, int P>
+__device__ __forceinline__ float routed_dot_lds_fp4(const uint4 (&wq)[GW], const ScaleBytes<P> (&sc)[GW / P],
+                                                    const uint32_t* xl, int g0) {
+  float acc = 0.f;
+#pragma unroll
+  for (int gi = 0; gi < GW; ++gi) {
+    const uint4* xp = reinterpret_cast<const uint4*>(xl + (g0 + gi) * 16);
+    uint32_t xs[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = xp[q];
+      xs[4 * q] = v.x; xs[4 * q + 1] = v.y; xs[4 * q + 2] = v.z; xs[4 * q + 3] = v.w;
+    }
+    uint4 w = wq[gi];
+    asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+    uint32_t sw = sc[gi / P].w;
+    asm volatile("" : "+v"(sw));
+    acc += e8m0_scaled(dot_group_fp4(w, xs), (sw >> (8 * (gi % P))) & 0xFFu);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return acc;
+}
+
 // Shared BF16 rows (CW chunks of 8 inputs from chunk c0 on) against an
 // activation staged in LDS as bf16 pairs (4 dwords per chunk).
 template <int CW>

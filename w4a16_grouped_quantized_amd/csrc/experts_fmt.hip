@@ -44,10 +44,6 @@ constexpr int kFmtStage = 8;
 __device__ __forceinline__ float fdot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_f, a), __builtin_bit_cast(bf16x2_f, b), c, false);
 }
-template <int BYTE>
-__device__ __forceinline__ uint32_t fp4x2_bf16(uint32_t v) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((int)v, 1.0f, BYTE));
-}
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_bf16(uint32_t v) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v, 1.0f, HI));

@@ -37,11 +37,13 @@ hipError_t launch_down(const Shape& s, const uint8_t* packed, const PackedLayout
 
 // The whole small-M layer in one launch (M*k <= kMaxUnits): with route, the
 // router, top-k and softmax too (ids and w are written); without, ids and w
-// are read.  rmsnorm only with route.
+// are read.  rmsnorm only with route.  mxfp4: the routed experts are MXFP4
+// in the tiled layout (launch_pack_mxfp4) instead of INT4.
 bool layer_supported(const Shape& s, int M);
 hipError_t launch_layer(const Shape& s, const uint8_t* packed, const PackedLayout& PL, const float* router_w,
                         const uint16_t* x, int M, bool route, bool rmsnorm, float eps, uint16_t* x_norm,
-                        int32_t* ids, float* w, uint16_t* out, uint8_t* ws, const WsLayout& L, hipStream_t st);
+                        int32_t* ids, float* w, uint16_t* out, uint8_t* ws, const WsLayout& L, hipStream_t st,
+                        bool mxfp4 = false);
 
 hipError_t launch_permute(const Shape& s, const int32_t* ids, int M, int32_t* counts, int32_t* offsets,
                           int32_t* perm, int32_t* ghist, int32_t* err, hipStream_t st);
@@ -66,6 +68,10 @@ hipError_t launch_pack(const Shape& s, const uint8_t* w13_q, const uint16_t* w13
                        const uint8_t* w2_q, const uint16_t* w2_s, const uint16_t* sh_w13,
                        const uint16_t* sh_w2, uint8_t* packed, const PackedLayout& P,
                        hipStream_t st);
+
+hipError_t launch_pack_mxfp4(const Shape& s, const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
+                             const uint8_t* w2_s, const uint16_t* sh_w13, const uint16_t* sh_w2, uint8_t* packed,
+                             const PackedLayout& P, hipStream_t st);
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 

@@ -274,7 +274,7 @@ constexpr int kLayerMaxTokens = 4;
 // function and in the same order as every other wavefront that normalises,
 // so every copy has the same bits), then gb[t * H/32 + g] the group
 // corrections of each.  Whole-workgroup call.
-template <int NI>
+template <int NI, bool GB = true>
 __device__ __forceinline__ void stage_tokens(const LayerArgs& A, int t0, int nt, uint32_t* xl, float* gb) {
   const ExpArgs& a = A.a;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -293,14 +293,17 @@ __device__ __forceinline__ void stage_tokens(const LayerArgs& A, int t0, int nt,
       reinterpret_cast<uint4*>(xl)[c] = reinterpret_cast<const uint4*>(a.x + (size_t)t0 * a.H)[c];
   }
   lds_sync();
-  const int GK = a.H / kGroup;
-  for (int j = tid; j < nt * GK; j += kBlock) gb[j] = group_bias_lds<false>(xl + (size_t)(j / GK) * HD, j % GK);
-  lds_sync();
+  if constexpr (GB) {
+    const int GK = a.H / kGroup;
+    for (int j = tid; j < nt * GK; j += kBlock) gb[j] = group_bias_lds<false>(xl + (size_t)(j / GK) * HD, j % GK);
+    lds_sync();
+  }
 }
 
 // Three workgroups per CU (at most 168 VGPRs, LDS within a third of the CU):
 // a decode grid fits on the device at once.
-template <int NI, int GWG, int PG, int CWG, int PD, int NPQ, int NSC, int DG>
+// F: the routed experts' format, 0 INT4 (bf16 scales), 1 MXFP4 (E8M0 scales).
+template <int F, int NI, int GWG, int PG, int CWG, int PD, int NPQ, int NSC, int DG>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void k_layer(const LayerArgs A) {
   extern __shared__ __align__(16) uint32_t dyn[];  // router keys [M][E], then the staged tokens
   __shared__ float red[kWavesPerBlock][kWave];
@@ -446,7 +449,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const uint32_t ev = read_epoch(A);
     const int idx = blk - G.gGU, u = idx / a.Tgu, b = idx % a.Tgu;
     const int GK = a.H / kGroup;
-    stage_tokens<NI>(A, 0, a.M, xl, gbias);
+    stage_tokens<NI, F == 0>(A, 0, a.M, xl, gbias);
     const uint32_t T = take_tag(A, ev, &tag_lds);
     LTRACE(1);
     // units: distinct valid experts in order of first occurrence (S <= 64);
@@ -490,10 +493,19 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     // the scales first, so that each group's product waits for its own
     // codes only (loads return in issue order)
     uint4 wq[GWG];
-    ScalePack<PG> sc[GWG / PG];
-    const uint16_t* sb = a.gu_s + (size_t)e * a.gu_s_stride + ((size_t)(b * (GK / PG) + g0 / PG) * kWave + lane) * PG;
+    // scale element size 2 (bf16) or 1 (E8M0); the strides count bf16 elements
+    const size_t sidx = ((size_t)(b * (GK / PG) + g0 / PG) * kWave + lane) * PG;
+    ScalePack<PG> sc[F == 0 ? GWG / PG : 1];
+    ScaleBytes<PG> scb[F == 1 ? GWG / PG : 1];
+    if constexpr (F == 0) {
+      const uint16_t* sb = a.gu_s + (size_t)e * a.gu_s_stride + sidx;
 #pragma unroll
-    for (int j = 0; j < GWG / PG; ++j) sc[j].load(sb + (size_t)j * kWave * PG);
+      for (int j = 0; j < GWG / PG; ++j) sc[j].load(sb + (size_t)j * kWave * PG);
+    } else {
+      const uint8_t* sb = reinterpret_cast<const uint8_t*>(a.gu_s) + (size_t)e * a.gu_s_stride * 2 + sidx;
+#pragma unroll
+      for (int j = 0; j < GWG / PG; ++j) scb[j].load(sb + (size_t)j * kWave * PG);
+    }
     __builtin_amdgcn_sched_barrier(0);
     LTRACE(4);
     const uint8_t* qb = a.gu_q + (size_t)e * a.gu_q_stride + ((size_t)(b * GK + g0) * kWave + lane) * 16;
@@ -505,8 +517,12 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       const int p = __ffsll((unsigned long long)m) - 1;
       m &= m - 1;
       const int tok = p / a.k;
-      red[wave][lane] = active ? routed_dot_lds<GWG, PG>(wq, sc, xl + (size_t)tok * (a.H / 2), gbias + tok * GK, g0, magic)
-                               : 0.f;
+      if constexpr (F == 0)
+        red[wave][lane] = active ? routed_dot_lds<GWG, PG>(wq, sc, xl + (size_t)tok * (a.H / 2), gbias + tok * GK, g0,
+                                                           magic)
+                                 : 0.f;
+      else
+        red[wave][lane] = active ? routed_dot_lds_fp4<GWG, PG>(wq, scb, xl + (size_t)tok * (a.H / 2), g0) : 0.f;
       lds_sync();
       if (wave == 0) {
         // h of the tile as fp16 under a power-of-two scale 2^sh chosen from
@@ -575,9 +591,11 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       for (int i = 0; i < NPQ; ++i) {
         const int j = q + Q * i, jj = j / GKD, g = j - jj * GKD;
         const int e = j < nrec ? lids[t * a.k + jj] : -1;
-        sdv[i] = id_ok(e, a.E) ? a.dn_s[(size_t)e * a.dn_s_stride + ((size_t)(tile * (GKD / PD) + g / PD) * kWave + lrow) * PD +
-                                        g % PD]
-                               : 0u;
+        const size_t si = ((size_t)(tile * (GKD / PD) + g / PD) * kWave + lrow) * PD + g % PD;
+        if constexpr (F == 0)
+          sdv[i] = id_ok(e, a.E) ? a.dn_s[(size_t)e * a.dn_s_stride + si] : 0u;
+        else
+          sdv[i] = id_ok(e, a.E) ? reinterpret_cast<const uint8_t*>(a.dn_s)[(size_t)e * a.dn_s_stride * 2 + si] : 0u;
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -671,7 +689,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
             uint4* dst = reinterpret_cast<uint4*>(hst[tid]);
 #pragma unroll
             for (int w = 0; w < 4; ++w) dst[w] = make_uint4(hw[4 * w], hw[4 * w + 1], hw[4 * w + 2], hw[4 * w + 3]);
-            hbias[tid] = -1032.0f * s;  // turns sum (1024 + u) h into sum (u - 8) h
+            hbias[tid] = F == 0 ? -1032.0f * s : 0.f;  // turns sum (1024 + u) h into sum (u - 8) h
             hexp[tid] = sh;
             rst = 2;
           }
@@ -702,15 +720,31 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
             // two accumulation chains (dwords 0-1 and 2-3), added at the end
             float pr[2] = {hbias[j], 0.f};
             const uint32_t wdw[4] = {wd[i].x, wd[i].y, wd[i].z, wd[i].w};
+            if constexpr (F == 0) {
 #pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4)
+              for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                  const uint32_t pair = ((wdw[d] >> (4 * k4)) & 0x000F000Fu) | magic;  // fp16 (1024 + u)
+                  pr[d >> 1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pair),
+                                                      __builtin_bit_cast(half2_t, hp[4 * d + k4]), pr[d >> 1], false);
+                }
+              acc += ldexpf((pr[0] + pr[1]) * bf16_to_f32(sdv[i]), hexp[j]) * lw[p];
+            } else {
+              // byte k4 of dword d: the E2M1 pair of inputs 8d+2k4, +1 as exact fp16
 #pragma unroll
               for (int d = 0; d < 4; ++d) {
-                const uint32_t pair = ((wdw[d] >> (4 * k4)) & 0x000F000Fu) | magic;  // fp16 (1024 + u)
-                pr[d >> 1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pair),
-                                                    __builtin_bit_cast(half2_t, hp[4 * d + k4]), pr[d >> 1], false);
+                const auto f = [&](uint32_t pair, int k4) {
+                  pr[d >> 1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pair),
+                                                      __builtin_bit_cast(half2_t, hp[4 * d + k4]), pr[d >> 1], false);
+                };
+                f(fp4x2_f16<0>(wdw[d]), 0);
+                f(fp4x2_f16<1>(wdw[d]), 1);
+                f(fp4x2_f16<2>(wdw[d]), 2);
+                f(fp4x2_f16<3>(wdw[d]), 3);
               }
-            acc += ldexpf((pr[0] + pr[1]) * bf16_to_f32(sdv[i]), hexp[j]) * lw[p];
+              acc += e8m0_scaled(pr[0] + pr[1], sdv[i], hexp[j]) * lw[p];
+            }
           }
         }
       }
@@ -769,9 +803,9 @@ bool layer_variant(const Shape& s, LayerVariant& v) {
 // The workgroups of a launch wait for one another, so the whole grid must be
 // resident at once: the launch is refused (and the caller takes the separate
 // kernels) when the device cannot hold it.
-template <int NI, int GWG, int PG, int CWG, int PD, int NPQ, int NSC, int DG>
+template <int F, int NI, int GWG, int PG, int CWG, int PD, int NPQ, int NSC, int DG>
 hipError_t run_layer(const LayerArgs& A, size_t lds, hipStream_t st) {
-  auto kern = k_layer<NI, GWG, PG, CWG, PD, NPQ, NSC, DG>;
+  auto kern = k_layer<F, NI, GWG, PG, CWG, PD, NPQ, NSC, DG>;
   int dev = 0, ncu = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
@@ -799,7 +833,8 @@ bool layer_supported(const Shape& s, int M) {
 
 hipError_t launch_layer(const Shape& s, const uint8_t* packed, const PackedLayout& PL, const float* router_w,
                         const uint16_t* x, int M, bool route, bool rmsnorm, float eps, uint16_t* x_norm,
-                        int32_t* ids, float* w, uint16_t* out, uint8_t* ws, const WsLayout& L, hipStream_t st) {
+                        int32_t* ids, float* w, uint16_t* out, uint8_t* ws, const WsLayout& L, hipStream_t st,
+                        bool mxfp4) {
   LayerVariant v;
   if (!layer_variant(s, v)) return hipErrorInvalidValue;
   LayerArgs A;
@@ -828,7 +863,8 @@ hipError_t launch_layer(const Shape& s, const uint8_t* packed, const PackedLayou
 #define LAYER_CASE(NI_, GWG_, PG_, CWG_, PD_, NPQ_, NSC_, DG_)                                              \
   if (v.NI == NI_ && v.GWG == GWG_ && v.PG == PG_ && v.CWG == CWG_ && v.PD == PD_ && v.NPQ == NPQ_ &&       \
       v.NSC == NSC_ && v.DG == DG_)                                                                          \
-    return run_layer<NI_, GWG_, PG_, CWG_, PD_, NPQ_, NSC_, DG_>(A, lds, st);
+    return mxfp4 ? run_layer<1, NI_, GWG_, PG_, CWG_, PD_, NPQ_, NSC_, DG_>(A, lds, st)                      \
+                 : run_layer<0, NI_, GWG_, PG_, CWG_, PD_, NPQ_, NSC_, DG_>(A, lds, st);
   LAYER_CASE(10, 20, 4, 20, 2, 6, 3, 24)
   LAYER_CASE(10, 20, 4, 0, 2, 6, 0, 24)
   LAYER_CASE(1, 2, 2, 2, 1, 1, 1, 2)

@@ -90,21 +90,26 @@ struct PackedLayout {
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Bytes of one expert's parts as stored (also their per-expert strides in
-// the plain checkpoint layout).
+// the plain checkpoint layout); SB is the bytes of one scale (2 for the
+// bf16 scales of INT4, 1 for the E8M0 scales of MXFP4).
 __host__ __device__ inline size_t gu_codes_bytes(int H, int I) { return (size_t)2 * I * H / 2; }
-__host__ __device__ inline size_t gu_scales_bytes(int H, int I) { return (size_t)2 * I * (H / kGroup) * 2; }
+__host__ __device__ inline size_t gu_scales_bytes(int H, int I, int SB = 2) { return (size_t)2 * I * (H / kGroup) * SB; }
 __host__ __device__ inline size_t dn_codes_bytes(int H, int I) { return (size_t)H * I / 2; }
-__host__ __device__ inline size_t dn_scales_bytes(int H, int I) { return (size_t)H * (I / kGroup) * 2; }
+__host__ __device__ inline size_t dn_scales_bytes(int H, int I, int SB = 2) { return (size_t)H * (I / kGroup) * SB; }
 
+// The routed experts in MXFP4 use the same tiles: a (tile, group, lane)
+// chunk holds the row-group's 16 bytes as the checkpoint stores them (byte
+// b of dword d: inputs 8d+2b in the low nibble, 8d+2b+1 in the high one),
+// and the E8M0 scales are packed like the bf16 ones, one byte each.
 __host__ __device__
-inline PackedLayout packed_layout(int H, int E, int I, int has_shared) {
+inline PackedLayout packed_layout(int H, int E, int I, int has_shared, int SB = 2) {
   PackedLayout L;
   auto a256 = [](size_t v) { return (v + 255) / 256 * 256; };
   L.gu_q = 0;
   L.gu_s = L.gu_q + a256(gu_codes_bytes(H, I));
-  L.dn_q = L.gu_s + a256(gu_scales_bytes(H, I));
+  L.dn_q = L.gu_s + a256(gu_scales_bytes(H, I, SB));
   L.dn_s = L.dn_q + a256(dn_codes_bytes(H, I));
-  const size_t block = L.dn_s + a256(dn_scales_bytes(H, I));
+  const size_t block = L.dn_s + a256(dn_scales_bytes(H, I, SB));
   L.gu_q_stride = L.gu_s_stride = L.dn_q_stride = L.dn_s_stride = block;
   size_t off = block * E;
   L.sh_gu = off; if (has_shared) off = (off + (size_t)2 * I * H * 2 + 255) / 256 * 256;

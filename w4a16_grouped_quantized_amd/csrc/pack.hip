@@ -6,6 +6,9 @@ namespace moe {
 
 // One thread per 16-byte output chunk (tile, group, lane) of one expert;
 // expert e's codes at src + e * sstride (plain) and dst + e * dstride.
+// INT4 codes are reordered inside the chunk (layout.hpp); MXFP4 codes are
+// copied as they are.
+template <bool INT4>
 __global__ void k_pack_codes(const uint8_t* __restrict__ src, size_t sstride, uint8_t* __restrict__ dst,
                              size_t dstride, int E, int N, int K, int is_gu, int I) {
   const int GK = K / kGroup, T = N / 64;
@@ -19,6 +22,11 @@ __global__ void k_pack_codes(const uint8_t* __restrict__ src, size_t sstride, ui
     const int b = (int)(r0 / ((size_t)kWave * GK));
     const int row = is_gu ? gu_row(b, l, I) : 64 * b + l;
     const uint8_t* s = src + (size_t)e * sstride + (size_t)row * (K / 2) + (size_t)g * 16;
+    uint4* out = reinterpret_cast<uint4*>(dst + (size_t)e * dstride + ((size_t)(b * GK + g) * kWave + l) * 16);
+    if constexpr (!INT4) {
+      *out = *reinterpret_cast<const uint4*>(s);
+      continue;
+    }
     uint32_t d[4];
 #pragma unroll
     for (int dw = 0; dw < 4; ++dw) {
@@ -31,14 +39,14 @@ __global__ void k_pack_codes(const uint8_t* __restrict__ src, size_t sstride, ui
       }
       d[dw] = v;
     }
-    *reinterpret_cast<uint4*>(dst + (size_t)e * dstride + ((size_t)(b * GK + g) * kWave + l) * 16) =
-        make_uint4(d[0], d[1], d[2], d[3]);
+    *out = make_uint4(d[0], d[1], d[2], d[3]);
   }
 }
 
 // One thread per (tile, pack of P groups, lane) of one expert; strides in
-// elements, as for k_pack_codes.
-__global__ void k_pack_scales(const uint16_t* __restrict__ src, size_t sstride, uint16_t* __restrict__ dst,
+// elements, as for k_pack_codes; S is the scale's type (bf16 bits or E8M0).
+template <typename S>
+__global__ void k_pack_scales(const S* __restrict__ src, size_t sstride, S* __restrict__ dst,
                               size_t dstride, int E, int N, int K, int is_gu, int I, int P) {
   const int GK = K / kGroup, T = N / 64, NP = GK / P;
   const size_t per_e = (size_t)T * NP * kWave;
@@ -50,8 +58,8 @@ __global__ void k_pack_scales(const uint16_t* __restrict__ src, size_t sstride, 
     const int gp = (int)((r0 / kWave) % NP);
     const int b = (int)(r0 / ((size_t)kWave * NP));
     const int row = is_gu ? gu_row(b, l, I) : 64 * b + l;
-    const uint16_t* s = src + (size_t)e * sstride + (size_t)row * GK + (size_t)gp * P;
-    uint16_t* d = dst + (size_t)e * dstride + ((size_t)(b * NP + gp) * kWave + l) * P;
+    const S* s = src + (size_t)e * sstride + (size_t)row * GK + (size_t)gp * P;
+    S* d = dst + (size_t)e * dstride + ((size_t)(b * NP + gp) * kWave + l) * P;
     for (int q = 0; q < P; ++q) d[q] = s[q];
   }
 }
@@ -171,19 +179,19 @@ hipError_t launch_pack(const Shape& s, const uint8_t* w13_q, const uint16_t* w13
   const KSplit kg = ksplit_for(H / kGroup), kd = ksplit_for(I / kGroup);
   hipError_t err;
   size_t n = (size_t)E * (2 * I / 64) * (H / kGroup) * kWave;
-  hipLaunchKernelGGL(k_pack_codes, dim3(grid_for(n)), dim3(256), 0, st, w13_q, gu_codes_bytes(H, I), packed + P.gu_q,
+  hipLaunchKernelGGL(k_pack_codes<true>, dim3(grid_for(n)), dim3(256), 0, st, w13_q, gu_codes_bytes(H, I), packed + P.gu_q,
                      P.gu_q_stride, E, 2 * I, H, 1, I);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   n = (size_t)E * (2 * I / 64) * (H / kGroup / kg.P) * kWave;
-  hipLaunchKernelGGL(k_pack_scales, dim3(grid_for(n)), dim3(256), 0, st, w13_s, gu_scales_bytes(H, I) / 2,
+  hipLaunchKernelGGL(k_pack_scales<uint16_t>, dim3(grid_for(n)), dim3(256), 0, st, w13_s, gu_scales_bytes(H, I) / 2,
                      reinterpret_cast<uint16_t*>(packed + P.gu_s), P.gu_s_stride / 2, E, 2 * I, H, 1, I, kg.P);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   n = (size_t)E * (H / 64) * (I / kGroup) * kWave;
-  hipLaunchKernelGGL(k_pack_codes, dim3(grid_for(n)), dim3(256), 0, st, w2_q, dn_codes_bytes(H, I), packed + P.dn_q,
+  hipLaunchKernelGGL(k_pack_codes<true>, dim3(grid_for(n)), dim3(256), 0, st, w2_q, dn_codes_bytes(H, I), packed + P.dn_q,
                      P.dn_q_stride, E, H, I, 0, I);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   n = (size_t)E * (H / 64) * (I / kGroup / kd.P) * kWave;
-  hipLaunchKernelGGL(k_pack_scales, dim3(grid_for(n)), dim3(256), 0, st, w2_s, dn_scales_bytes(H, I) / 2,
+  hipLaunchKernelGGL(k_pack_scales<uint16_t>, dim3(grid_for(n)), dim3(256), 0, st, w2_s, dn_scales_bytes(H, I) / 2,
                      reinterpret_cast<uint16_t*>(packed + P.dn_s), P.dn_s_stride / 2, E, H, I, 0, I, kd.P);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   uint32_t* meta = reinterpret_cast<uint32_t*>(packed + P.meta);
@@ -212,6 +220,46 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
   hipLaunchKernelGGL(k_fill_zero, dim3(grid_for(n16)), dim3(256), 0, st, reinterpret_cast<uint4*>(p), n16,
                      reinterpret_cast<uint8_t*>(p) + n16 * 16, tail);
   return hipGetLastError();
+}
+
+// MXFP4 routed experts into the same tiles (codes as stored, E8M0 scale
+// bytes packed like the bf16 scales); the shared BF16 expert as for INT4.
+// The range data of the many-token path is left zero: the MXFP4 layout
+// serves the one-launch layer only.
+hipError_t launch_pack_mxfp4(const Shape& s, const uint8_t* w13_q, const uint8_t* w13_s, const uint8_t* w2_q,
+                             const uint8_t* w2_s, const uint16_t* sh_w13, const uint16_t* sh_w2, uint8_t* packed,
+                             const PackedLayout& P, hipStream_t st) {
+  const int H = s.H, I = s.I, E = s.E;
+  const KSplit kg = ksplit_for(H / kGroup), kd = ksplit_for(I / kGroup);
+  hipError_t err;
+  size_t n = (size_t)E * (2 * I / 64) * (H / kGroup) * kWave;
+  hipLaunchKernelGGL(k_pack_codes<false>, dim3(grid_for(n)), dim3(256), 0, st, w13_q, gu_codes_bytes(H, I),
+                     packed + P.gu_q, P.gu_q_stride, E, 2 * I, H, 1, I);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  n = (size_t)E * (2 * I / 64) * (H / kGroup / kg.P) * kWave;
+  hipLaunchKernelGGL(k_pack_scales<uint8_t>, dim3(grid_for(n)), dim3(256), 0, st, w13_s, gu_scales_bytes(H, I, 1),
+                     packed + P.gu_s, P.gu_s_stride, E, 2 * I, H, 1, I, kg.P);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  n = (size_t)E * (H / 64) * (I / kGroup) * kWave;
+  hipLaunchKernelGGL(k_pack_codes<false>, dim3(grid_for(n)), dim3(256), 0, st, w2_q, dn_codes_bytes(H, I),
+                     packed + P.dn_q, P.dn_q_stride, E, H, I, 0, I);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  n = (size_t)E * (H / 64) * (I / kGroup / kd.P) * kWave;
+  hipLaunchKernelGGL(k_pack_scales<uint8_t>, dim3(grid_for(n)), dim3(256), 0, st, w2_s, dn_scales_bytes(H, I, 1),
+                     packed + P.dn_s, P.dn_s_stride, E, H, I, 0, I, kd.P);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  if ((err = launch_fill_zero(packed + P.meta, (size_t)E * kMetaWords * 4, st)) != hipSuccess) return err;
+  if (s.has_shared) {
+    n = (size_t)(2 * I / 64) * (H / 8) * kWave;
+    hipLaunchKernelGGL(k_pack_bf16, dim3(grid_for(n)), dim3(256), 0, st, sh_w13,
+                       reinterpret_cast<uint16_t*>(packed + P.sh_gu), 2 * I, H, 1, I);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    n = (size_t)(H / 64) * (I / 8) * kWave;
+    hipLaunchKernelGGL(k_pack_bf16, dim3(grid_for(n)), dim3(256), 0, st, sh_w2,
+                       reinterpret_cast<uint16_t*>(packed + P.sh_dn), H, I, 0, I);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 }  // namespace moe
