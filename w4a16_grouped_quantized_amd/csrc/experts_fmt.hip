@@ -85,26 +85,28 @@ __device__ __forceinline__ float chunk_dot(uint4 w, const uint32_t* x) {
 template <int F>
 constexpr int chunk_cols() { return F == kFmtMxfp4 ? 32 : (F == kFmtFp8Block ? 16 : 8); }
 
-// Scale of chunk c of row n (the factor its chunk_dot is multiplied by),
-// requested with the codes; MXFP4 keeps the E8M0 exponent, applied with ldexp.
+// Scale of chunk c of row n (what its chunk_dot is multiplied by), as raw
+// bits: the E8M0 byte for MXFP4, the fp32 bits for FP8.  Requested with the
+// codes and decoded only where it is used, so that no instruction needs the
+// loaded value (and waits for it) before the next chunk's requests.
 template <int F>
-__device__ __forceinline__ float chunk_scale(const FmtMat& m, int n, int c) {
+__device__ __forceinline__ uint32_t chunk_scale(const FmtMat& m, int n, int c) {
   if constexpr (F == kFmtMxfp4) {
-    return (float)reinterpret_cast<const uint8_t*>(m.s)[(size_t)n * (m.K / 32) + c];
+    return reinterpret_cast<const uint8_t*>(m.s)[(size_t)n * (m.K / 32) + c];
   } else if constexpr (F == kFmtFp8Block) {
     const int kb = (m.K + 127) / 128;
-    return reinterpret_cast<const float*>(m.s)[(size_t)(n / 128) * kb + (c * 16) / 128];
+    return reinterpret_cast<const uint32_t*>(m.s)[(size_t)(n / 128) * kb + (c * 16) / 128];
   } else {
-    return 1.0f;
+    return 0u;
   }
 }
 template <int F>
-__device__ __forceinline__ float scaled(float dot, float sc) {
+__device__ __forceinline__ float scaled(float dot, uint32_t sc) {
   if constexpr (F == kFmtMxfp4) {
     const int e = (int)sc;
     return e == 255 ? __builtin_nanf("") : __builtin_amdgcn_ldexpf(dot, e - 127);
   } else {
-    return dot * sc;
+    return dot * __uint_as_float(sc);
   }
 }
 template <int F>
@@ -191,18 +193,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   const int cpr = shared ? H / chunk_cols<kFmtBf16>() : H / chunk_cols<FB>();
   const int nch = rows * cpr;
   uint4 w[NC];
-  float sc[NC];
+  uint32_t sc[NC];
 #pragma unroll
   for (int i = 0; i < NC; ++i) {
     const int j = tid + 256 * i;
-    sc[i] = 0.f;
+    sc[i] = 0u;
     w[i] = make_uint4(0, 0, 0, 0);
     if (j < nch) {
       const int rl = j / cpr, c = j % cpr;
       const int n = rl < half ? g0 + rl : I + g0 + (rl - half);
       if (shared) {
         w[i] = chunk_load<kFmtBf16>(m, n, c);
-        sc[i] = 1.f;
       } else {
         sc[i] = chunk_scale<FB>(m, n, c);
         w[i] = chunk_load<FB>(m, n, c);
@@ -331,68 +332,72 @@ __global__ __launch_bounds__(256) void k_fmt_down(const FmtArgs A) {
   }
   constexpr int lgf = hwf == 16 ? 4 : (hwf == 8 ? 3 : 2);  // log2 of a chunk's dwords
   uint4 w[NC];
-  float sc[NC];
-#pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    w[i] = make_uint4(0, 0, 0, 0);
-    sc[i] = 0.f;
-  }
+  uint32_t sc[NC];
+  const size_t rowbytes = F == kFmtMxfp4 ? (size_t)I / 2 : (size_t)I;
+  const uint8_t* shq = reinterpret_cast<const uint8_t*>(A.sh_w2);
+  const int q4 = I / 4, n4 = nseg * q4;  // h: I dwords per segment (I/2 hi, I/2 lo)
   for (int t = 0; t < M; ++t) {
+    // h (hi, lo) of the token's slots and of the shared expert, and the slot
+    // weights, requested first and without a branch (an index past the end
+    // reads entry 0 and is not stored): they come from the workspace, and a
+    // wait for them then does not also wait for the weight stream requested
+    // after them (nseg * I / 4 <= 256 * kFmtStage)
+    uint4 hv[kFmtStage];
+#pragma unroll
+    for (int m2 = 0; m2 < kFmtStage; ++m2) {
+      const int i4 = tid + 256 * m2 < n4 ? tid + 256 * m2 : 0;
+      const int seg = i4 / q4, d4 = i4 - seg * q4;
+      const int slot = seg < k ? t * k + seg : S + t;
+      hv[m2] = reinterpret_cast<const uint4*>(A.hb + (size_t)slot * 2 * I)[d4];
+    }
+    const float lwv = A.topk_w[t * k + tid % k];
+    // every chunk's two requests with no branch around them: a chunk that
+    // adds nothing (none, or an id out of range) reads a valid address of
+    // expert 0 and is dropped when the products are formed.  A load under a
+    // branch whose result merges with another value makes the wave wait for
+    // it before the next request; here all of them are in flight at once.
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       const int ci = cinfo[i];
-      if (ci < 0) continue;
-      const int seg = ci >> 17, n = n0 + ((ci >> 10) & 127), c = ci & 1023;
-      if (seg < k) {
-        const int e = sid[t * k + seg];
-        sc[i] = 0.f;
-        w[i] = make_uint4(0, 0, 0, 0);
-        if (e >= 0 && e < A.E) {
-          FmtMat m{A.w2_q + (size_t)e * A.w2_q_stride, A.w2_s + (size_t)e * A.w2_s_stride, I};
-          sc[i] = chunk_scale<F>(m, n, c);
-          w[i] = chunk_load<F>(m, n, c);
-        }
-      } else if (t == 0) {
-        FmtMat m{reinterpret_cast<const uint8_t*>(A.sh_w2), nullptr, I};
-        w[i] = chunk_load<kFmtBf16>(m, n, c);
+      const int cv = ci < 0 ? 0 : ci;
+      const int seg = cv >> 17, n = n0 + ((cv >> 10) & 127), c = cv & 1023;
+      const bool routed = seg < k;
+      const int e0 = sid[t * k + (routed ? seg : 0)];
+      const int e = (e0 >= 0 && e0 < A.E) ? e0 : 0;
+      // 32-bit byte offsets (fmt_plan checks that every matrix fits): a
+      // 64-bit multiply-add here ends up reading the register pair of a
+      // load still in flight, which makes the wave wait for it
+      const uint32_t qoff = routed ? (uint32_t)e * (uint32_t)A.w2_q_stride + (uint32_t)n * (uint32_t)rowbytes
+                                   : (uint32_t)n * (uint32_t)(I * 2);
+      w[i] = *reinterpret_cast<const uint4*>((routed ? A.w2_q : shq) + qoff + (uint32_t)c * 16u);
+      const int cs = routed ? c : 0;
+      if constexpr (F == kFmtMxfp4) {
+        sc[i] = A.w2_s[(uint32_t)e * (uint32_t)A.w2_s_stride + (uint32_t)n * (uint32_t)(I / 32) + (uint32_t)cs];
+      } else {
+        const int kb = (I + 127) / 128;
+        sc[i] = *reinterpret_cast<const uint32_t*>(A.w2_s + (uint32_t)e * (uint32_t)A.w2_s_stride +
+                                                   (uint32_t)((n / 128) * kb + (cs * 16) / 128) * 4u);
       }
     }
-    // the token's slot weights (0 for an id out of range), and h (hi, lo) of
-    // its slots and of the shared expert
+    // the slot weights (0 for an id out of range) and h into LDS
     if (tid < k) {
       const int e = sid[t * k + tid];
-      lw[tid] = (e >= 0 && e < A.E) ? A.topk_w[t * k + tid] : 0.f;
+      lw[tid] = (e >= 0 && e < A.E) ? lwv : 0.f;
     }
-    {
-      // I dwords per segment (I/2 hi, I/2 lo), as 16-byte loads all requested
-      // before the first is stored (nseg * I / 4 <= 256 * kFmtStage)
-      const int q4 = I / 4, n4 = nseg * q4;
-      uint4 v[kFmtStage];
 #pragma unroll
-      for (int m2 = 0; m2 < kFmtStage; ++m2) {
-        const int i4 = tid + 256 * m2;
-        v[m2] = make_uint4(0, 0, 0, 0);
-        if (i4 < n4) {
-          const int seg = i4 / q4, d4 = i4 - seg * q4;
-          const int slot = seg < k ? t * k + seg : S + t;
-          v[m2] = reinterpret_cast<const uint4*>(A.hb + (size_t)slot * 2 * I)[d4];
-        }
-      }
+    for (int m2 = 0; m2 < kFmtStage; ++m2) {
+      const int i4 = tid + 256 * m2;
+      if (i4 < n4) {
+        const int seg = i4 / q4, d4 = i4 - seg * q4;
+        const bool lo = 4 * d4 >= I / 2;
+        const int dd0 = 4 * d4 - (lo ? I / 2 : 0);
+        const int lg = seg < k ? lgf : 2;  // 4 dwords per BF16 chunk
+        uint32_t* dst = (lo ? hlo : hhi) + seg * segf;
+        const uint32_t dv[4] = {hv[m2].x, hv[m2].y, hv[m2].z, hv[m2].w};
 #pragma unroll
-      for (int m2 = 0; m2 < kFmtStage; ++m2) {
-        const int i4 = tid + 256 * m2;
-        if (i4 < n4) {
-          const int seg = i4 / q4, d4 = i4 - seg * q4;
-          const bool lo = 4 * d4 >= I / 2;
-          const int dd0 = 4 * d4 - (lo ? I / 2 : 0);
-          const int lg = seg < k ? lgf : 2;  // 4 dwords per BF16 chunk
-          uint32_t* dst = (lo ? hlo : hhi) + seg * segf;
-          const uint32_t dv[4] = {v[m2].x, v[m2].y, v[m2].z, v[m2].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int dd = dd0 + e;  // 4 consecutive dwords stay in one chunk
-            dst[(dd >> lg) * ((1 << lg) + 1) + (dd & ((1 << lg) - 1))] = dv[e];
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int dd = dd0 + e;  // 4 consecutive dwords stay in one chunk
+          dst[(dd >> lg) * ((1 << lg) + 1) + (dd & ((1 << lg) - 1))] = dv[e];
         }
       }
     }
@@ -410,7 +415,9 @@ __global__ __launch_bounds__(256) void k_fmt_down(const FmtArgs A) {
       if (ci >= 0) {
         const int seg = ci >> 17, r = (ci >> 10) & 127, c = ci & 1023;
         float v;
-        if (seg < k) {
+        if (seg < k && (unsigned)sid[t * k + seg] >= (unsigned)A.E) {
+          v = 0.f;  // an id out of range adds nothing
+        } else if (seg < k) {
           // the hi half, then the lo half (one set of inputs in registers)
           const uint32_t* hp = hhi + seg * segf + c * pdf;
           uint32_t xs[hwf];
@@ -473,6 +480,8 @@ hipError_t run_fmt(const FmtArgs& A, hipStream_t st) {
 bool fmt_plan(const Shape& s, int fmt, int M, int* ra, int* rsh, int* rb) {
   if (fmt != kFmtMxfp4 && fmt != kFmtFp8Block) return false;
   const int cols = fmt == kFmtMxfp4 ? 32 : 16;
+  // the down kernel addresses a matrix with 32-bit byte offsets
+  if ((uint64_t)s.E * s.H * s.I >= ((uint64_t)1 << 32)) return false;
   if (s.H % 32 || s.I % 32 || M < 1 || M * s.k > kMaxUnits) return false;
   if ((int64_t)(s.k + 1) * 2 * s.I * 2 > (int64_t)s.k * s.H * 4) return false;  // h fits the down-partials buffer
   const int cpa = s.H / cols, cps = s.H / 8;
