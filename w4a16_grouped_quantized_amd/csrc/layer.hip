@@ -513,16 +513,23 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     for (int i = 0; i < GWG; ++i) wq[i] = *reinterpret_cast<const uint4*>(qb + (size_t)i * kWave * 16);
     const uint32_t magic = bf16_pair_magic();
     LTRACE(5);
-    while (m) {
-      const int p = __ffsll((unsigned long long)m) - 1;
-      m &= m - 1;
-      const int tok = p / a.k;
+    auto dot_member = [&](int tok) -> float {
       if constexpr (F == 0)
-        red[wave][lane] = active ? routed_dot_lds<GWG, PG>(wq, sc, xl + (size_t)tok * (a.H / 2), gbias + tok * GK, g0,
-                                                           magic)
-                                 : 0.f;
+        return active ? routed_dot_lds<GWG, PG>(wq, sc, xl + (size_t)tok * (a.H / 2), gbias + tok * GK, g0, magic)
+                      : 0.f;
       else
-        red[wave][lane] = active ? routed_dot_lds_fp4<GWG, PG>(wq, scb, xl + (size_t)tok * (a.H / 2), g0) : 0.f;
+        return active ? routed_dot_lds_fp4<GWG, PG>(wq, scb, xl + (size_t)tok * (a.H / 2), g0) : 0.f;
+    };
+    // The first member's products come right after the requests, outside
+    // the loop over members: the compiler then waits for each group's codes
+    // as the products reach them, where a loop entry would make it wait for
+    // all of them first.  A decode unit has one member, so the loop body
+    // never computes.
+    int p = __ffsll((unsigned long long)m) - 1;
+    m &= m - 1;
+    float dv = dot_member(p / a.k);
+    for (;;) {
+      red[wave][lane] = dv;
       lds_sync();
       if (wave == 0) {
         // h of the tile as fp16 under a power-of-two scale 2^sh chosen from
@@ -547,6 +554,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         if (lane == 0) st_coherent(&A.hmeta[rec], tagged((uint32_t)sh, T));
       }
       lds_sync();
+      if (!m) break;
+      p = __ffsll((unsigned long long)m) - 1;
+      m &= m - 1;
+      dv = dot_member(p / a.k);
     }
     LTRACE_WAIT();
     LTRACE(6);
