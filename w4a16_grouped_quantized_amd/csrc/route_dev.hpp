@@ -357,15 +357,22 @@ template <int NI>
 __device__ __forceinline__ void router_row(const RouteArgs& a, int e, int lane, bool writer, uint32_t* keys = nullptr) {
   const bool has_row = e < a.E;
   const int er = has_row ? e : a.E - 1;
+  constexpr int kRouteBatch = 4;
+  // the first batch of tokens is requested with the router row (one round
+  // trip for both; inside the token loop it would follow the row)
+  uint2 batch[kRouteBatch][NI];
+#pragma unroll
+  for (int b = 0; b < kRouteBatch; ++b)
+    if (b < a.M) fetch_token<NI>(a.x + (size_t)b * a.H, lane, batch[b]);
   float4 wr[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) wr[i] = *reinterpret_cast<const float4*>(a.wr + (size_t)er * a.H + 256 * i + 4 * lane);
-  constexpr int kRouteBatch = 4;
   for (int t0 = 0; t0 < a.M; t0 += kRouteBatch) {
-    uint2 batch[kRouteBatch][NI];
+    if (t0 > 0) {
 #pragma unroll
-    for (int b = 0; b < kRouteBatch; ++b)
-      if (t0 + b < a.M) fetch_token<NI>(a.x + (size_t)(t0 + b) * a.H, lane, batch[b]);
+      for (int b = 0; b < kRouteBatch; ++b)
+        if (t0 + b < a.M) fetch_token<NI>(a.x + (size_t)(t0 + b) * a.H, lane, batch[b]);
+    }
 #pragma unroll
     for (int b = 0; b < kRouteBatch; ++b) {
       const int t = t0 + b;
