@@ -54,11 +54,8 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(const ExpArgs a) {
     const uint16_t* sb = a.gu_s + (size_t)e * a.gu_s_stride + ((size_t)(b * (GK / P) + g0 / P) * kWave + lane) * P;
 #pragma unroll
     for (int j = 0; j < GW / P; ++j) sc[j].load(sb + (size_t)j * kWave * P);
-    for (int c = 0; c < U.nmem; ++c) {
-      if (c > 0) {
-        p = member_slot(a.S, c, m, L);
-        if (tid < GK) gb.load(a.x + (size_t)(p / a.k) * a.H, tid);
-      }
+    // one member (slot p routed to this expert): h of tile b for its token
+    auto member = [&](int p) {
       const uint16_t* act = a.x + (size_t)(p / a.k) * a.H;
       if (tid < GK) L.bias[tid] = gb.value();
       lds_sync();
@@ -72,6 +69,14 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(const ExpArgs a) {
         store_hilo(a.h + ((size_t)p * a.I + 32 * b) * 2, tid, silu_f32(g) * up);
       }
       lds_sync();
+    };
+    // the first member outside the loop: its products then wait for each
+    // group's codes as they reach them, not for all of them at a loop entry
+    member(p);
+    for (int c = 1; c < U.nmem; ++c) {
+      p = member_slot(a.S, c, m, L);
+      if (tid < GK) gb.load(a.x + (size_t)(p / a.k) * a.H, tid);
+      member(p);
     }
     return;
   }
@@ -152,11 +157,7 @@ __global__ __launch_bounds__(kBlock) void k_down(const ExpArgs a) {
       const uint16_t* sb = a.dn_s + (size_t)e * a.dn_s_stride + ((size_t)(b * (GK / P) + g0 / P) * kWave + lane) * P;
 #pragma unroll
       for (int j = 0; j < GW / P; ++j) sc[j].load(sb + (size_t)j * kWave * P);
-      for (int c = 0; c < U.nmem; ++c) {
-        if (c > 0) {
-          p = member_slot(a.S, c, m, L);
-          if (tid < GK) gb.load(a.h + (size_t)p * a.I * 2, tid);
-        }
+      auto member = [&](int p) {
         const uint16_t* act = a.h + (size_t)p * a.I * 2;
         if (tid < GK) L.bias[tid] = gb.value();
         lds_sync();
@@ -169,6 +170,13 @@ __global__ __launch_bounds__(kBlock) void k_down(const ExpArgs a) {
           st_coherent(&a.dpart[(size_t)p * a.H + 64 * b + tid], part * a.topk_w[p]);
         }
         lds_sync();
+      };
+      // the first member outside the loop, as in k_gate_up
+      member(p);
+      for (int c = 1; c < U.nmem; ++c) {
+        p = member_slot(a.S, c, m, L);
+        if (tid < GK) gb.load(a.h + (size_t)p * a.I * 2, tid);
+        member(p);
       }
     }
   } else if constexpr (CW == 0) {
