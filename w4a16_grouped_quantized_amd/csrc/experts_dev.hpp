@@ -284,6 +284,56 @@ __device__ __forceinline__ float routed_dot_lds(const uint4 (&wq)[GW], const Sca
   return acc;
 }
 
+// routed_dot_lds against the fp16 copy of a staged token (to_fp16_tokens):
+// xh holds the inputs times 2^-r as fp16 pairs in natural order, the pairs
+// of odd dwords divided by 16 once more; bias the matching group
+// corrections.  Under the fp16 exponent of 1024 a code at bits 0-3 of a
+// half is the exact value 1024 + u, and one at bits 4-7 the exact value
+// 1024 + 16 u (fp16 keeps 10 mantissa bits), so of a code dword's four pairs
+// (inputs 2i, 2i+1 at nibbles i and 4 + i) pairs 0 and 1 come straight from
+// the dword and pairs 2 and 3 from it shifted by 8: five instructions per
+// dword where bf16 (7 mantissa bits) needs seven.  The odd pairs' extra
+// factor 16 is the one their inputs were divided by.  Returns the sum
+// times 2^-r.
+template <int GW, int P>
+__device__ __forceinline__ float routed_dot_lds_h(const uint4 (&wq)[GW], const ScalePack<P> (&sc)[GW / P],
+                                                  const uint32_t* xh, const float* bias, int g0, uint32_t magic16) {
+  float acc = 0.f;
+#pragma unroll
+  for (int gi = 0; gi < GW; ++gi) {
+    const uint4* xp = reinterpret_cast<const uint4*>(xh + (g0 + gi) * 16);
+    uint32_t xs[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 v = xp[q];
+      xs[4 * q] = v.x; xs[4 * q + 1] = v.y; xs[4 * q + 2] = v.z; xs[4 * q + 3] = v.w;
+    }
+    // opaque copies, as in routed_dot_lds
+    uint4 w = wq[gi];
+    asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+    uint32_t sw = sc[gi / P].w[(gi % P) >> 1];
+    asm volatile("" : "+v"(sw));
+    const float scale = ((gi % P) & 1) ? __uint_as_float(sw & 0xFFFF0000u) : __uint_as_float(sw << 16);
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+    float pr = bias[g0 + gi];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t t = wd[d] >> 8;
+      const auto f = [&](uint32_t pair, uint32_t x) {
+        pr = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pair), __builtin_bit_cast(half2_t, x), pr, false);
+      };
+      f((wd[d] & 0x000F000Fu) | magic16, xs[4 * d]);
+      f((wd[d] & 0x00F000F0u) | magic16, xs[4 * d + 1]);
+      f((t & 0x000F000Fu) | magic16, xs[4 * d + 2]);
+      f((t & 0x00F000F0u) | magic16, xs[4 * d + 3]);
+    }
+    acc = fmaf(scale, pr, acc);
+    // one group's activation reads in flight at a time
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return acc;
+}
+
 // ---- MXFP4 routed experts (tiled layout, codes as the checkpoint stores
 // them, E8M0 scale bytes packed P per lane-load)
 

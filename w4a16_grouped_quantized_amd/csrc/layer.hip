@@ -300,6 +300,53 @@ __device__ __forceinline__ void stage_tokens(const LayerArgs& A, int t0, int nt,
   }
 }
 
+// The routed role's tokens as fp16, in place of the staged bf16 pairs: token
+// t's inputs times 2^-r_t (r_t puts the largest magnitude below 2^15; bf16's
+// 8 significant bits fit fp16's 11, so the copy is exact down to fp16's
+// normal range, 2^-29 of the largest input), the pairs of odd dwords divided
+// by 16 more (see routed_dot_lds_h), and in gb the group corrections
+// -1032 (sum of the even dwords' values) - 1152 (sum of the odd dwords'),
+// which turn the products with 1024 + u and 1024 + 16 u into products with
+// the codes u - 8.  xexp[t] = r_t.  Whole-workgroup call.
+__device__ __forceinline__ void to_fp16_tokens(int nt, int H, uint32_t* xl, float* gb, int* xexp,
+                                               float (*red)[kWave]) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int HD = H / 2, GK = H / kGroup;
+  for (int t = 0; t < nt; ++t) {
+    uint32_t* x = xl + (size_t)t * HD;
+    float m = 0.f;
+    for (int c = tid; c < HD; c += kBlock)
+      m = fmaxf(m, fmaxf(fabsf(bf16_to_f32(x[c] & 0xFFFFu)), fabsf(bf16_to_f32(x[c] >> 16))));
+    m = wave_max(m);
+    if (lane == 0) red[wave][0] = m;
+    lds_sync();
+    m = fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0]));
+    int e = 0;
+    frexpf(m, &e);  // m < 2^e
+    const int r = e - 15;
+    for (int c = tid; c < HD; c += kBlock) {
+      const int sh = (c & 1) ? -r - 4 : -r;
+      const _Float16 lo = (_Float16)ldexpf(bf16_to_f32(x[c] & 0xFFFFu), sh);
+      const _Float16 hi = (_Float16)ldexpf(bf16_to_f32(x[c] >> 16), sh);
+      x[c] = __builtin_bit_cast(uint32_t, (half2_t){lo, hi});
+    }
+    if (tid == 0) xexp[t] = r;
+    lds_sync();
+    for (int g = tid; g < GK; g += kBlock) {
+      float se = 0.f, so = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; j += 2) {
+        const half2_t ve = __builtin_bit_cast(half2_t, x[16 * g + j]);
+        const half2_t vo = __builtin_bit_cast(half2_t, x[16 * g + j + 1]);
+        se += (float)ve[0] + (float)ve[1];
+        so += (float)vo[0] + (float)vo[1];
+      }
+      gb[t * GK + g] = -1032.0f * se - 1152.0f * so;
+    }
+    lds_sync();
+  }
+}
+
 // Three workgroups per CU (at most 168 VGPRs, LDS within a third of the CU):
 // a decode grid fits on the device at once.
 // F: the routed experts' format, 0 INT4 (bf16 scales), 1 MXFP4 (E8M0 scales).
@@ -309,6 +356,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   __shared__ float red[kWavesPerBlock][kWave];
   __shared__ int flag;
   __shared__ uint32_t tag_lds;
+  __shared__ int xexp[kLayerMaxTokens];  // routed role: exponents of the fp16 tokens
   __shared__ __align__(16) int topk_lds[kWavesPerBlock * kTopkLdsInts];
   __shared__ int lids[kMaxUnits];
   __shared__ float lw[kMaxUnits];
@@ -449,7 +497,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const uint32_t ev = read_epoch(A);
     const int idx = blk - G.gGU, u = idx / a.Tgu, b = idx % a.Tgu;
     const int GK = a.H / kGroup;
-    stage_tokens<NI, F == 0>(A, 0, a.M, xl, gbias);
+    stage_tokens<NI, false>(A, 0, a.M, xl, gbias);
+    if constexpr (F == 0) to_fp16_tokens(a.M, a.H, xl, gbias, xexp, red);
     const uint32_t T = take_tag(A, ev, &tag_lds);
     LTRACE(1);
     // units: distinct valid experts in order of first occurrence (S <= 64);
@@ -511,11 +560,13 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const uint8_t* qb = a.gu_q + (size_t)e * a.gu_q_stride + ((size_t)(b * GK + g0) * kWave + lane) * 16;
 #pragma unroll
     for (int i = 0; i < GWG; ++i) wq[i] = *reinterpret_cast<const uint4*>(qb + (size_t)i * kWave * 16);
-    const uint32_t magic = bf16_pair_magic();
+    const uint32_t magic16 = fp16_pair_magic();
     LTRACE(5);
     auto dot_member = [&](int tok) -> float {
       if constexpr (F == 0)
-        return active ? routed_dot_lds<GWG, PG>(wq, sc, xl + (size_t)tok * (a.H / 2), gbias + tok * GK, g0, magic)
+        return active ? ldexpf(routed_dot_lds_h<GWG, PG>(wq, sc, xl + (size_t)tok * (a.H / 2), gbias + tok * GK, g0,
+                                                         magic16),
+                               xexp[tok])
                       : 0.f;
       else
         return active ? routed_dot_lds_fp4<GWG, PG>(wq, scb, xl + (size_t)tok * (a.H / 2), g0) : 0.f;
