@@ -295,7 +295,9 @@ __device__ __forceinline__ float routed_dot_lds(const uint4 (&wq)[GW], const Sca
 // dword where bf16 (7 mantissa bits) needs seven.  The odd pairs' extra
 // factor 16 is the one their inputs were divided by.  Returns the sum
 // times 2^-r.
-template <int GW, int P>
+// OPQ: the opaque copies of routed_dot_lds, for calls inside a loop over
+// tokens (a call outside any loop has nothing to be hoisted out of).
+template <int GW, int P, bool OPQ = true>
 __device__ __forceinline__ float routed_dot_lds_h(const uint4 (&wq)[GW], const ScalePack<P> (&sc)[GW / P],
                                                   const uint32_t* xh, const float* bias, int g0, uint32_t magic16) {
   float acc = 0.f;
@@ -308,11 +310,12 @@ __device__ __forceinline__ float routed_dot_lds_h(const uint4 (&wq)[GW], const S
       const uint4 v = xp[q];
       xs[4 * q] = v.x; xs[4 * q + 1] = v.y; xs[4 * q + 2] = v.z; xs[4 * q + 3] = v.w;
     }
-    // opaque copies, as in routed_dot_lds
     uint4 w = wq[gi];
-    asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
     uint32_t sw = sc[gi / P].w[(gi % P) >> 1];
-    asm volatile("" : "+v"(sw));
+    if constexpr (OPQ) {  // opaque copies, as in routed_dot_lds
+      asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+      asm volatile("" : "+v"(sw));
+    }
     const float scale = ((gi % P) & 1) ? __uint_as_float(sw & 0xFFFF0000u) : __uint_as_float(sw << 16);
     const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
     float pr = bias[g0 + gi];

@@ -49,6 +49,7 @@
 // them; and a product waits for every load issued before its operands, so
 // each role requests its scales before its codes.
 #include <algorithm>
+#include <type_traits>
 
 #include "experts_dev.hpp"
 #include "route_dev.hpp"
@@ -562,10 +563,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     for (int i = 0; i < GWG; ++i) wq[i] = *reinterpret_cast<const uint4*>(qb + (size_t)i * kWave * 16);
     const uint32_t magic16 = fp16_pair_magic();
     LTRACE(5);
-    auto dot_member = [&](int tok) -> float {
+    auto dot_member = [&](int tok, auto first) -> float {
       if constexpr (F == 0)
-        return active ? ldexpf(routed_dot_lds_h<GWG, PG>(wq, sc, xl + (size_t)tok * (a.H / 2), gbias + tok * GK, g0,
-                                                         magic16),
+        return active ? ldexpf(routed_dot_lds_h<GWG, PG, !decltype(first)::value>(
+                                   wq, sc, xl + (size_t)tok * (a.H / 2), gbias + tok * GK, g0, magic16),
                                xexp[tok])
                       : 0.f;
       else
@@ -578,7 +579,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     // never computes.
     int p = __ffsll((unsigned long long)m) - 1;
     m &= m - 1;
-    float dv = dot_member(p / a.k);
+    float dv = dot_member(p / a.k, std::true_type{});
     for (;;) {
       red[wave][lane] = dv;
       lds_sync();
@@ -608,7 +609,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       if (!m) break;
       p = __ffsll((unsigned long long)m) - 1;
       m &= m - 1;
-      dv = dot_member(p / a.k);
+      dv = dot_member(p / a.k, std::false_type{});
     }
     LTRACE_WAIT();
     LTRACE(6);
