@@ -599,7 +599,10 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         int ex = 0;
         frexpf(mx, &ex);
         const int sh = mx > 0.f ? ex - 15 : 0;  // |h| * 2^-sh < 2^15
-        const uint32_t hb = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(v, -sh));
+        // INT4: the values of odd dwords (lanes 2-3 mod 4) divided by 16 more,
+        // for the down role's shift-free pairs (see routed_dot_lds_h)
+        const int odd = F == 0 ? ((lane >> 1) & 1) : 0;
+        const uint32_t hb = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(v, -sh - 4 * odd));
         const uint32_t nb = (uint32_t)__shfl_down((int)hb, 1, 64);
         const size_t rec = (size_t)p * a.Tgu + b;
         if (lane < 32 && !(lane & 1)) st_coherent(&A.hval[rec * 16 + lane / 2], tagged(hb | (nb << 16), T));
@@ -742,17 +745,23 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
             }
           }
           if (ok) {
-            float s = 0.f;
+            float se = 0.f, so = 0.f;
 #pragma unroll
-            for (int w = 0; w < 16; ++w) {
-              const half2_t h2 = __builtin_bit_cast(half2_t, hw[w]);
-              s += (float)h2[0];
-              s += (float)h2[1];
+            for (int w = 0; w < 16; w += 2) {
+              const half2_t he = __builtin_bit_cast(half2_t, hw[w]);
+              const half2_t ho = __builtin_bit_cast(half2_t, hw[w + 1]);
+              se += (float)he[0];
+              se += (float)he[1];
+              so += (float)ho[0];
+              so += (float)ho[1];
             }
             uint4* dst = reinterpret_cast<uint4*>(hst[tid]);
 #pragma unroll
             for (int w = 0; w < 4; ++w) dst[w] = make_uint4(hw[4 * w], hw[4 * w + 1], hw[4 * w + 2], hw[4 * w + 3]);
-            hbias[tid] = F == 0 ? -1032.0f * s : 0.f;  // turns sum (1024 + u) h into sum (u - 8) h
+            // turns the products with 1024 + u (even dwords) and 1024 + 16 u
+            // (odd dwords, whose h is stored divided by 16) into products
+            // with u - 8
+            hbias[tid] = F == 0 ? -1032.0f * se - 1152.0f * so : 0.f;
             hexp[tid] = sh;
             rst = 2;
           }
@@ -784,14 +793,19 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
             float pr[2] = {hbias[j], 0.f};
             const uint32_t wdw[4] = {wd[i].x, wd[i].y, wd[i].z, wd[i].w};
             if constexpr (F == 0) {
+              // nibbles 0, 4 and 1, 5 of each code dword straight from it,
+              // 2, 6 and 3, 7 from it shifted by 8: fp16 (1024 + u) and
+              // (1024 + 16 u) pairs, as in routed_dot_lds_h
 #pragma unroll
-              for (int k4 = 0; k4 < 4; ++k4)
+              for (int d = 0; d < 4; ++d) {
+                const uint32_t t8 = wdw[d] >> 8;
+                const uint32_t pairs[4] = {(wdw[d] & 0x000F000Fu) | magic, (wdw[d] & 0x00F000F0u) | magic,
+                                           (t8 & 0x000F000Fu) | magic, (t8 & 0x00F000F0u) | magic};
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                  const uint32_t pair = ((wdw[d] >> (4 * k4)) & 0x000F000Fu) | magic;  // fp16 (1024 + u)
-                  pr[d >> 1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pair),
+                for (int k4 = 0; k4 < 4; ++k4)
+                  pr[d >> 1] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pairs[k4]),
                                                       __builtin_bit_cast(half2_t, hp[4 * d + k4]), pr[d >> 1], false);
-                }
+              }
               acc += ldexpf((pr[0] + pr[1]) * bf16_to_f32(sdv[i]), hexp[j]) * lw[p];
             } else {
               // byte k4 of dword d: the E2M1 pair of inputs 8d+2k4, +1 as exact fp16
