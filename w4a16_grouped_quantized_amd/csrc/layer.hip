@@ -431,6 +431,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     gather_keys(A, T, lkeys);
     LTRACE(1);
     select_slots(A, lkeys, topk_lds, lids, lw);
+    LTRACE(3);
     uint64_t* rec = A.rrec + (size_t)c * 2 * kMaxUnits;
     for (int p = tid; p < a.S; p += kBlock) {
       st_coherent(&rec[p], tagged((uint32_t)lids[p], T));

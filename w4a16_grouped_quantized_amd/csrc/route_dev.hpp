@@ -226,6 +226,10 @@ __device__ __forceinline__ void topk_select_small(const uint32_t (&key)[kTopkEPL
     const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b[j] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b[j], 0u));
     cand[c[j] ? pre[j] + below : kWave + lane] = ((uint64_t)kv[j] << 32) | (uint32_t)(0xFFFF - (lane + kWave * j));
   }
+  // zeros after the C candidates up to the next multiple of 16 (a zero is
+  // below every candidate: keys are never 0), so the ranking below reads
+  // whole blocks of 16 without a bound check per entry
+  if (lane < 16) cand[C + lane] = 0ull;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
@@ -237,8 +241,8 @@ __device__ __forceinline__ void topk_select_small(const uint32_t (&key)[kTopkEPL
     for (int q = 0; q < 8; ++q) v[q] = reinterpret_cast<const ulonglong2*>(cand)[i0 / 2 + q];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      rank += (i0 + 2 * q < C && v[q].x > mine) ? 1 : 0;
-      rank += (i0 + 2 * q + 1 < C && v[q].y > mine) ? 1 : 0;
+      rank += v[q].x > mine ? 1 : 0;
+      rank += v[q].y > mine ? 1 : 0;
     }
   }
   uint64_t* res = cand + 2 * kWave;
