@@ -428,9 +428,20 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const uint32_t ev = read_epoch(A);
     const uint32_t T = take_tag(A, ev, &tag_lds);
     const int c = blk - G.gSL;
-    gather_keys(A, T, lkeys);
-    LTRACE(1);
-    select_slots(A, lkeys, topk_lds, lids, lw);
+    // The top-k runs twice, the same instructions both times: first on
+    // stand-in keys (distinct, so it takes its usual path) while the router
+    // rows are still being computed, which brings its code into the
+    // instruction cache, then on the call's keys.
+    for (int i = tid; i < a.M * a.E; i += kBlock) lkeys[i] = (uint32_t)(i + 1);
+    lds_sync();
+#pragma unroll 1
+    for (int pass = 0; pass < 2; ++pass) {
+      if (pass == 1) {
+        gather_keys(A, T, lkeys);
+        LTRACE(1);
+      }
+      select_slots(A, lkeys, topk_lds, lids, lw);
+    }
     LTRACE(3);
     uint64_t* rec = A.rrec + (size_t)c * 2 * kMaxUnits;
     for (int p = tid; p < a.S; p += kBlock) {
