@@ -290,7 +290,9 @@ def roofline_steps(ctx, r, path):
     """Roofline of the dominant kernel of a decode/verify/stack measurement."""
     M = r["tokens_per_step"]
     stack = r["workload"] == WORKLOAD_NAMES["stack"]
-    one_launch = path == "layer" and M == 1
+    # moe_layer_w4a16 takes the one launch for M <= 2 (k_layer), the
+    # separate kernels above
+    one_launch = path == "layer" and M <= 2
     if one_launch:
         # k_layer is the only kernel, one launch per layer step
         launches = STACK_LAYERS if stack else 1

@@ -162,19 +162,19 @@ int moe_forward_w4a16(const moe_config* cfg /* host */, const void* packed, cons
 
 /* flag for moe_layer_w4a16 */
 #define MOE_F_ONE_LAUNCH 0x2u  /* use the one-launch kernel for every M it supports
-                                  (M <= 4 and M*top_k <= 64), not only for M = 1 */
+                                  (M <= 4 and M*top_k <= 64), not only for M <= 2 */
 
 /* One whole MoE layer for a step of M tokens (a Ling-3.0-flash MoE layer's
  * routed experts and shared expert, as moe_route and moe_forward_w4a16
  * define them): moe_route followed by
  * moe_forward_w4a16 on the ids and weights it produced (topk_ids, topk_w,
  * x_norm and out are all written; ids, weights and x_norm are those of
- * moe_route bit for bit).  For one token (decode) the router, the top-k and
- * the expert FFNs run as one launch whose routed weight loads start as soon
- * as the experts are chosen; its output agrees with the two calls' within
- * their rounding (the expert h is kept as scaled fp16 instead of a bf16
- * pair).  Otherwise it is the two calls, unless MOE_F_ONE_LAUNCH asks for the
- * one launch.  flags: MOE_F_INPUT_RMSNORM as for moe_route (the experts then
+ * moe_route bit for bit).  For one or two tokens (decode, a verify step of
+ * one draft) the router, the top-k and the expert FFNs run as one launch
+ * whose routed weight loads start as soon as the experts are chosen; its
+ * output agrees with the two calls' within their rounding (the expert h is
+ * kept as scaled fp16 instead of a bf16 pair).  Otherwise it is the two
+ * calls, unless MOE_F_ONE_LAUNCH asks for the one launch.  flags: MOE_F_INPUT_RMSNORM as for moe_route (the experts then
  * see x_norm, which must not overlap x), MOE_F_ONE_LAUNCH.  Concurrent calls
  * on one workspace race.  The single launch stands in for the pages' CUDA
  * graphs, which cut the per-kernel launch cost that dominates when few
@@ -300,9 +300,9 @@ int moe_forward_fmt(const moe_config* cfg /* host */, int32_t fmt, const moe_wei
  *   MOE_F_INPUT_RMSNORM); ids and weights equal moe_route's bit for bit and
  *   out agrees with moe_route + moe_forward_fmt on the plain weights within
  *   their rounding (h kept as scaled fp16).  Only the shapes and token counts
- *   the one-launch layer covers (M <= 4, M * top_k <= 64, a grid the device
- *   holds at once): MOE_ERR_UNSUPPORTED otherwise, with nothing launched;
- *   use moe_route + moe_forward_fmt there. */
+ *   the one-launch layer covers (M <= 4, M * top_k <= 64, a device that holds
+ *   at least two of its workgroups at once): MOE_ERR_UNSUPPORTED otherwise,
+ *   with nothing launched; use moe_route + moe_forward_fmt there. */
 size_t moe_packed_size_mxfp4(const moe_config* cfg /* host */);
 int moe_pack_weights_mxfp4(const moe_config* cfg /* host */, const moe_weights_fmt* src /* host struct */,
                            void* packed, size_t packed_bytes, void* stream);

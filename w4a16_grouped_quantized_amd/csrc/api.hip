@@ -228,7 +228,7 @@ int moe_layer_w4a16(const moe_config* cfg, const float* router_w, const void* pa
   if (M < 0 || (flags & ~(MOE_F_INPUT_RMSNORM | MOE_F_ONE_LAUNCH))) return MOE_ERR_SHAPE;
   if (M == 0) return MOE_OK;
   const bool rms = (flags & MOE_F_INPUT_RMSNORM) != 0;
-  const bool one = M == 1 || (flags & MOE_F_ONE_LAUNCH) != 0;
+  const bool one = M <= 2 || (flags & MOE_F_ONE_LAUNCH) != 0;
   if (!router_w || !packed || !x || !topk_ids || !topk_w || !out || !ws || (rms && !x_norm)) return MOE_ERR_NULL;
   if (!aligned16(router_w) || !aligned16(packed) || !aligned16(x) || !aligned16(out) || !aligned16(ws) ||
       !aligned4(topk_ids) || !aligned4(topk_w) || (rms && !aligned16(x_norm)))

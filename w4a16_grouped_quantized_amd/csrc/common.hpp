@@ -40,22 +40,24 @@ constexpr int kRouteCounters = 1 + (512 / 4 + kArriveFan - 1) / kArriveFan;
 // (4 per workgroup) and selectors (the top-k, published in kSelectors
 // copies), both only when the launch routes, shared gate_up (tile x K
 // slice), routed gate_up (slot x gate_up tile; slots past the number of
-// distinct experts have nothing to do), down (kDnRows output rows each:
-// every routed and the shared down projection of those rows, and the
-// output).  S = M*k (token, slot) pairs bound the distinct-expert units.
+// distinct experts have nothing to do), down (kDnRows output rows each, of
+// every token or of one: every routed and the shared down projection of
+// those rows, and the output).  S = M*k (token, slot) pairs bound the distinct-expert units.
 struct LayerGrid {
   int gSL, gSG, gGU, gDN, grid;  // router rows: workgroups 1 .. gSL-1; selectors gSL .. gSG-1
 };
 constexpr int kDnRows = 8;
 constexpr int kSelectors = 8;
-inline LayerGrid layer_roles(int H, int E, int I, int has_shared, int route, int M, int k) {
+// per_token: one down workgroup per (row block, token) instead of one per
+// row block walking the tokens.
+inline LayerGrid layer_roles(int H, int E, int I, int has_shared, int route, int M, int k, int per_token) {
   const SharedSplit sg = shared_gu_split(H);
   LayerGrid g;
   g.gSL = 1 + (route ? (E + 3) / 4 : 0);
   g.gSG = g.gSL + (route ? kSelectors : 0);
   g.gGU = g.gSG + (has_shared ? (I / 32) * sg.KS : 0);
   g.gDN = g.gGU + M * k * (I / 32);
-  g.grid = g.gDN + H / kDnRows;
+  g.grid = g.gDN + (H / kDnRows) * (per_token ? M : 1);
   return g;
 }
 

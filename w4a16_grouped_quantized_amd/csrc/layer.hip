@@ -23,7 +23,8 @@
 //                   u's expert and compute h of the tile's 32 rows for every
 //                   token routed to it, stored as fp16 pairs under a
 //                   power-of-two scale, with the tag;
-//   down            (8 output rows): reads a routing record, requests the
+//   down            (8 output rows, of every token, or of one when M >= 2):
+//                   reads a routing record, requests the
 //                   down rows of every slot's expert (the shared expert's at
 //                   the start), then polls the shared h and the h records and
 //                   writes out = sum_slots w * (W_down h) + W_shared_down h_sh.
@@ -37,10 +38,14 @@
 // exception is the leader (workgroup 0), which waits for every other
 // workgroup's arrival before it advances the epoch; no workgroup waits for
 // the leader.  So the grid makes progress as long as one workgroup slot
-// besides the leader's is free and workgroups are dispatched in id order;
-// the host also refuses the launch unless the device can hold the whole grid
-// at once.  Each poll is bounded and records bit 1 of the error word if it
-// gives up.  Words crossing workgroups are stored agent-coherently (written
+// besides the leader's is free and each XCD takes its workgroups in id
+// order: the unfinished workgroup with the smallest id (the leader aside)
+// waits only for finished ones, and if it is not resident yet, every
+// workgroup ahead of it on its XCD has finished and left a slot.  A decode
+// grid (M = 1) fits on the device at once; at M >= 2 the later down
+// workgroups take the slots that the router rows, the selectors and the
+// routed gate_up workgroups leave.  Each poll is bounded and records bit 1
+// of the error word if it gives up.  Words crossing workgroups are stored agent-coherently (written
 // through past the XCD's L2, which is not coherent with the others) and
 // polled with agent-coherent loads; a 64-bit word is stored and loaded whole,
 // so its tag and payload always belong together.  Vector loads return in
@@ -351,7 +356,9 @@ __device__ __forceinline__ void to_fp16_tokens(int nt, int H, uint32_t* xl, floa
 // Three workgroups per CU (at most 168 VGPRs, LDS within a third of the CU):
 // a decode grid fits on the device at once.
 // F: the routed experts' format, 0 INT4 (bf16 scales), 1 MXFP4 (E8M0 scales).
-template <int F, int NI, int GWG, int PG, int CWG, int PD, int NPQ, int NSC, int DG>
+// PT: one down workgroup per (row block, token) (M >= 2); otherwise each
+// down workgroup walks the tokens of its rows.
+template <int F, int NI, int GWG, int PG, int CWG, int PD, int NPQ, int NSC, int DG, bool PT>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) void k_layer(const LayerArgs A) {
   extern __shared__ __align__(16) uint32_t dyn[];  // router keys [M][E], then the staged tokens
   __shared__ float red[kWavesPerBlock][kWave];
@@ -634,11 +641,17 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
   // ------------------------------------------------------------ down
   // rows row0 .. row0+7: thread (row, q) takes the (slot, group) pairs
   // j = q + 32 i of a token and the shared chunks q + 32 c, and the 32
-  // partial sums of a row are added in q order.
+  // partial sums of a row are added in q order.  With PT each workgroup
+  // takes one token of its rows, and the M workgroups of a row block have
+  // ids 8 apart, so they run on one XCD (ids are dealt to the XCDs in
+  // turn), whose L2 then serves the shared expert's down rows to all but
+  // the first.
   {
     constexpr int Q = kBlock / kDnRows;
     const uint32_t ev = read_epoch(A);
-    const int r = blk - G.gDN;
+    const int idx = blk - G.gDN;
+    const int r = PT ? ((idx >> 3) / a.M) * 8 + (idx & 7) : idx;
+    const int t_first = PT ? (idx >> 3) % a.M : 0, t_end = PT ? t_first + 1 : a.M;
     const int row = tid % kDnRows, q = tid / kDnRows;
     const int row0 = r * kDnRows, tile = row0 >> 6, lrow = (row0 & 63) + row;
     constexpr int GKD = DG;  // I / 32
@@ -657,9 +670,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     if (wave == 0) routing_wave(A, T, r % kSelectors, lane, lids, lw, true);
     lds_sync();
     LTRACE(3);
-    if (!A.route && r == 0 && tid < a.S && !id_ok(lids[tid], a.E)) atomicOr(a.err, 1);
+    if (!A.route && idx == 0 && tid < a.S && !id_ok(lids[tid], a.E)) atomicOr(a.err, 1);
     const int nrec = a.k * GKD;  // (slot, group) records of one token, <= Q * NPQ
-    for (int t = 0; t < a.M; ++t) {
+    for (int t = t_first; t < t_end; ++t) {
       // this token's down rows of every slot's expert: the scales first,
       // so that the first record's product waits for its own codes only
       // (loads return in issue order)
@@ -885,23 +898,26 @@ bool layer_variant(const Shape& s, LayerVariant& v) {
                     v.NPQ == 6 && (v.NSC == 0 || v.NSC == 3) && v.DG == 24;
   const bool tiny = v.NI == 1 && v.GWG == 2 && v.PG == 2 && (v.CWG == 0 || v.CWG == 2) && v.PD == 1 && v.NPQ == 1 &&
                     (v.NSC == 0 || v.NSC == 1) && v.DG == 2;
-  // every record of a token is staged by one thread
-  return (ling || tiny) && (v.CWG == 0) == (v.NSC == 0) && s.k * (s.I / kGroup) <= kBlock;
+  // every record of a token is staged by one thread; the down workgroups
+  // of one row block sit 8 ids apart
+  return (ling || tiny) && (v.CWG == 0) == (v.NSC == 0) && s.k * (s.I / kGroup) <= kBlock &&
+         (s.H / kDnRows) % 8 == 0;
 }
 
-// The workgroups of a launch wait for one another, so the whole grid must be
-// resident at once: the launch is refused (and the caller takes the separate
-// kernels) when the device cannot hold it.
-template <int F, int NI, int GWG, int PG, int CWG, int PD, int NPQ, int NSC, int DG>
+// The workgroups of a launch wait for one another; a grid larger than the
+// device holds at once still completes (see the file comment), but the
+// launch is refused (and the caller takes the separate kernels) unless the
+// device holds the leader and one more workgroup.
+template <int F, int NI, int GWG, int PG, int CWG, int PD, int NPQ, int NSC, int DG, bool PT>
 hipError_t run_layer(const LayerArgs& A, size_t lds, hipStream_t st) {
-  auto kern = k_layer<F, NI, GWG, PG, CWG, PD, NPQ, NSC, DG>;
+  auto kern = k_layer<F, NI, GWG, PG, CWG, PD, NPQ, NSC, DG, PT>;
   int dev = 0, ncu = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern), kBlock, lds) !=
           hipSuccess)
     return hipErrorInvalidValue;
-  if ((int64_t)per_cu * ncu < A.g.grid) return hipErrorInvalidConfiguration;
+  if ((int64_t)per_cu * ncu < 2) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(kern, dim3(A.g.grid), dim3(kBlock), lds, st, A);
   return hipGetLastError();
 }
@@ -938,7 +954,8 @@ hipError_t launch_layer(const Shape& s, const uint8_t* packed, const PackedLayou
   r.ids = ids; r.w = w;
   A.route = route ? 1 : 0;
   A.rmsnorm = rmsnorm ? 1 : 0;
-  A.g = layer_roles(s.H, s.E, s.I, s.has_shared, route ? 1 : 0, M, s.k);
+  const bool pt = M > 1;
+  A.g = layer_roles(s.H, s.E, s.I, s.has_shared, route ? 1 : 0, M, s.k, pt ? 1 : 0);
   A.epoch = reinterpret_cast<uint32_t*>(ws + L.epoch);
   A.arrive = reinterpret_cast<int32_t*>(ws + L.arrive);
   A.rkeys = reinterpret_cast<uint64_t*>(ws + L.rkeys);
@@ -952,8 +969,10 @@ hipError_t launch_layer(const Shape& s, const uint8_t* packed, const PackedLayou
 #define LAYER_CASE(NI_, GWG_, PG_, CWG_, PD_, NPQ_, NSC_, DG_)                                              \
   if (v.NI == NI_ && v.GWG == GWG_ && v.PG == PG_ && v.CWG == CWG_ && v.PD == PD_ && v.NPQ == NPQ_ &&       \
       v.NSC == NSC_ && v.DG == DG_)                                                                          \
-    return mxfp4 ? run_layer<1, NI_, GWG_, PG_, CWG_, PD_, NPQ_, NSC_, DG_>(A, lds, st)                      \
-                 : run_layer<0, NI_, GWG_, PG_, CWG_, PD_, NPQ_, NSC_, DG_>(A, lds, st);
+    return mxfp4 ? (pt ? run_layer<1, NI_, GWG_, PG_, CWG_, PD_, NPQ_, NSC_, DG_, true>(A, lds, st)           \
+                       : run_layer<1, NI_, GWG_, PG_, CWG_, PD_, NPQ_, NSC_, DG_, false>(A, lds, st))         \
+                 : (pt ? run_layer<0, NI_, GWG_, PG_, CWG_, PD_, NPQ_, NSC_, DG_, true>(A, lds, st)           \
+                       : run_layer<0, NI_, GWG_, PG_, CWG_, PD_, NPQ_, NSC_, DG_, false>(A, lds, st));
   LAYER_CASE(10, 20, 4, 20, 2, 6, 3, 24)
   LAYER_CASE(10, 20, 4, 0, 2, 6, 0, 24)
   LAYER_CASE(1, 2, 2, 2, 1, 1, 1, 2)
