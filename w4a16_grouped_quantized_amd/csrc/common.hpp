@@ -313,6 +313,19 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return h0 + h1;
 }
 
+// The largest v of the wavefront, in every lane, by the same row moves as
+// wave_sum_dpp (no LDS round trip per step).
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_move<0xB1>(v));
+  v = fmaxf(v, dpp_move<0x4E>(v));
+  v = fmaxf(v, dpp_move<0x141>(v));
+  v = fmaxf(v, dpp_move<0x140>(v));
+  v = fmaxf(v, __uint_as_float((uint32_t)__builtin_amdgcn_ds_swizzle((int)__float_as_uint(v), 0x401F)));
+  const float h0 = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 0));
+  const float h1 = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), 32));
+  return fmaxf(h0, h1);
+}
+
 // Two floats to a bf16 pair (round to nearest even), in one instruction.
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {

@@ -323,7 +323,7 @@ __device__ __forceinline__ void to_fp16_tokens(int nt, int H, uint32_t* xl, floa
     float m = 0.f;
     for (int c = tid; c < HD; c += kBlock)
       m = fmaxf(m, fmaxf(fabsf(bf16_to_f32(x[c] & 0xFFFFu)), fabsf(bf16_to_f32(x[c] >> 16))));
-    m = wave_max(m);
+    m = wave_max_dpp(m);
     if (lane == 0) red[wave][0] = m;
     lds_sync();
     m = fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0]));
@@ -612,9 +612,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
           for (int w = 0; w < kWavesPerBlock; ++w) { gt += red[w][lane]; up += red[w][lane + 32]; }
           v = silu_f32(gt) * up;
         }
-        float mx = fabsf(v);
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+        const float mx = wave_max_dpp(fabsf(v));
         int ex = 0;
         frexpf(mx, &ex);
         const int sh = mx > 0.f ? ex - 15 : 0;  // |h| * 2^-sh < 2^15
@@ -622,7 +620,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
         // for the down role's shift-free pairs (see routed_dot_lds_h)
         const int odd = F == 0 ? ((lane >> 1) & 1) : 0;
         const uint32_t hb = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(v, -sh - 4 * odd));
-        const uint32_t nb = (uint32_t)__shfl_down((int)hb, 1, 64);
+        // the odd neighbour's half (quad_perm [1,1,3,3])
+        const uint32_t nb = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hb, 0xF5, 0xF, 0xF, false);
         const size_t rec = (size_t)p * a.Tgu + b;
         if (lane < 32 && !(lane & 1)) st_coherent(&A.hval[rec * 16 + lane / 2], tagged(hb | (nb << 16), T));
         if (lane == 0) st_coherent(&A.hmeta[rec], tagged((uint32_t)sh, T));
