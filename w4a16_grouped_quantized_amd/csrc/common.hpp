@@ -313,6 +313,18 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return h0 + h1;
 }
 
+// 16 bytes of a weight stream, read once per launch: a non-temporal load, so
+// the bytes pass the CU's vector cache without being kept there.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float4 ld_stream_f4(const float* p) {
+  const uint4 v = ld_stream(p);
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w));
+}
+
 // The largest v of the wavefront, in every lane, by the same row moves as
 // wave_sum_dpp (no LDS round trip per step).
 __device__ __forceinline__ float wave_max_dpp(float v) {

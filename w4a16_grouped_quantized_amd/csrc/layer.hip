@@ -398,7 +398,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     const int er = has_row ? e : a.E - 1;
     float4 wr[NI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) wr[i] = *reinterpret_cast<const float4*>(A.r.wr + (size_t)er * a.H + 256 * i + 4 * lane);
+    for (int i = 0; i < NI; ++i) wr[i] = ld_stream_f4(A.r.wr + (size_t)er * a.H + 256 * i + 4 * lane);
     // the logits of every token first (red[wave][t]), then the tag
     for (int t = 0; t < a.M; ++t) {
       float xv[NI][4];
@@ -477,7 +477,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       uint4 wc[CWG];
       const uint8_t* base = reinterpret_cast<const uint8_t*>(a.sh_gu) + ((size_t)(b * (a.H / 8) + c0) * kWave + lane) * 16;
 #pragma unroll
-      for (int c = 0; c < CWG; ++c) wc[c] = *reinterpret_cast<const uint4*>(base + (size_t)c * kWave * 16);
+      for (int c = 0; c < CWG; ++c) wc[c] = ld_stream(base + (size_t)c * kWave * 16);
       stage_tokens<NI>(A, 0, a.M, xl, gbias);
       for (int t = 0; t < a.M; ++t) {
         red[wave][lane] = shared_dot_lds<CWG>(wc, xl + (size_t)t * (a.H / 2), c0);
@@ -579,7 +579,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
     LTRACE(4);
     const uint8_t* qb = a.gu_q + (size_t)e * a.gu_q_stride + ((size_t)(b * GK + g0) * kWave + lane) * 16;
 #pragma unroll
-    for (int i = 0; i < GWG; ++i) wq[i] = *reinterpret_cast<const uint4*>(qb + (size_t)i * kWave * 16);
+    for (int i = 0; i < GWG; ++i) wq[i] = ld_stream(qb + (size_t)i * kWave * 16);
     const uint32_t magic16 = fp16_pair_magic();
     LTRACE(5);
     auto dot_member = [&](int tok, auto first) -> float {
@@ -660,8 +660,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
 #pragma unroll
       for (int c = 0; c < NSC; ++c) {
         const int cc = q + Q * c;
-        wsh[c] = cc < a.I / 8 ? *reinterpret_cast<const uint4*>(reinterpret_cast<const uint8_t*>(a.sh_dn) +
-                                                                  ((size_t)(tile * (a.I / 8) + cc) * kWave + lrow) * 16)
+        wsh[c] = cc < a.I / 8 ? ld_stream(reinterpret_cast<const uint8_t*>(a.sh_dn) +
+                                          ((size_t)(tile * (a.I / 8) + cc) * kWave + lrow) * 16)
                               : make_uint4(0, 0, 0, 0);
       }
     }
@@ -692,8 +692,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(3))) voi
       for (int i = 0; i < NPQ; ++i) {
         const int j = q + Q * i, jj = j / GKD, g = j - jj * GKD;
         const int e = j < nrec ? lids[t * a.k + jj] : -1;
-        wd[i] = id_ok(e, a.E) ? *reinterpret_cast<const uint4*>(a.dn_q + (size_t)e * a.dn_q_stride +
-                                                               ((size_t)(tile * GKD + g) * kWave + lrow) * 16)
+        wd[i] = id_ok(e, a.E) ? ld_stream(a.dn_q + (size_t)e * a.dn_q_stride +
+                                          ((size_t)(tile * GKD + g) * kWave + lrow) * 16)
                               : make_uint4(0, 0, 0, 0);
       }
       LTRACE(5);
