@@ -50,7 +50,7 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(const ExpArgs a) {
     ScalePack<P> sc[GW / P];
     const uint8_t* qb = a.gu_q + (size_t)e * a.gu_q_stride + ((size_t)(b * GK + g0) * kWave + lane) * 16;
 #pragma unroll
-    for (int i = 0; i < GW; ++i) wq[i] = *reinterpret_cast<const uint4*>(qb + (size_t)i * kWave * 16);
+    for (int i = 0; i < GW; ++i) wq[i] = ld_stream(qb + (size_t)i * kWave * 16);
     const uint16_t* sb = a.gu_s + (size_t)e * a.gu_s_stride + ((size_t)(b * (GK / P) + g0 / P) * kWave + lane) * P;
 #pragma unroll
     for (int j = 0; j < GW / P; ++j) sc[j].load(sb + (size_t)j * kWave * P);
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kBlock) void k_gate_up(const ExpArgs a) {
     const uint8_t* base = reinterpret_cast<const uint8_t*>(a.sh_gu) +
                           ((size_t)(b * (a.H / 8) + c0) * kWave + lane) * 16;
 #pragma unroll
-    for (int c = 0; c < CW; ++c) wc[c] = *reinterpret_cast<const uint4*>(base + (size_t)c * kWave * 16);
+    for (int c = 0; c < CW; ++c) wc[c] = ld_stream(base + (size_t)c * kWave * 16);
     for (int t = 0; t < a.M; ++t) {
       L.red[wave][lane] = shared_dot<CW, false>(wc, a.x + (size_t)t * a.H, c0);
       lds_sync();
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kBlock) void k_down(const ExpArgs a) {
       ScalePack<P> sc[GW / P];
       const uint8_t* qb = a.dn_q + (size_t)e * a.dn_q_stride + ((size_t)(b * GK + g0) * kWave + lane) * 16;
 #pragma unroll
-      for (int i = 0; i < GW; ++i) wq[i] = *reinterpret_cast<const uint4*>(qb + (size_t)i * kWave * 16);
+      for (int i = 0; i < GW; ++i) wq[i] = ld_stream(qb + (size_t)i * kWave * 16);
       const uint16_t* sb = a.dn_s + (size_t)e * a.dn_s_stride + ((size_t)(b * (GK / P) + g0 / P) * kWave + lane) * P;
 #pragma unroll
       for (int j = 0; j < GW / P; ++j) sc[j].load(sb + (size_t)j * kWave * P);
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(kBlock) void k_down(const ExpArgs a) {
     const uint8_t* base = reinterpret_cast<const uint8_t*>(a.sh_dn) +
                           ((size_t)(b * (a.I / 8) + c0) * kWave + lane) * 16;
 #pragma unroll
-    for (int c = 0; c < CW; ++c) wc[c] = *reinterpret_cast<const uint4*>(base + (size_t)c * kWave * 16);
+    for (int c = 0; c < CW; ++c) wc[c] = ld_stream(base + (size_t)c * kWave * 16);
     for (int t = 0; t < a.M; ++t) {
       L.red[wave][lane] = shared_dot<CW, true>(wc, a.h_sh + (size_t)t * a.I * 2, c0);
       lds_sync();

@@ -112,7 +112,7 @@ __device__ __forceinline__ float scaled(float dot, uint32_t sc) {
 template <int F>
 __device__ __forceinline__ uint4 chunk_load(const FmtMat& m, int n, int c) {
   const size_t rowbytes = F == kFmtMxfp4 ? (size_t)m.K / 2 : (F == kFmtFp8Block ? (size_t)m.K : (size_t)m.K * 2);
-  return *reinterpret_cast<const uint4*>(m.q + (size_t)n * rowbytes + (size_t)c * 16);
+  return ld_stream(m.q + (size_t)n * rowbytes + (size_t)c * 16);
 }
 
 // Sum of values[r * stride + c] over c < n for rows r < rows, into fn(r, sum):
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(256) void k_fmt_down(const FmtArgs A) {
       // load still in flight, which makes the wave wait for it
       const uint32_t qoff = routed ? (uint32_t)e * (uint32_t)A.w2_q_stride + (uint32_t)n * (uint32_t)rowbytes
                                    : (uint32_t)n * (uint32_t)(I * 2);
-      w[i] = *reinterpret_cast<const uint4*>((routed ? A.w2_q : shq) + qoff + (uint32_t)c * 16u);
+      w[i] = ld_stream((routed ? A.w2_q : shq) + qoff + (uint32_t)c * 16u);
       const int cs = routed ? c : 0;
       if constexpr (F == kFmtMxfp4) {
         sc[i] = A.w2_s[(uint32_t)e * (uint32_t)A.w2_s_stride + (uint32_t)n * (uint32_t)(I / 32) + (uint32_t)cs];

@@ -370,7 +370,7 @@ __device__ __forceinline__ void router_row(const RouteArgs& a, int e, int lane, 
     if (b < a.M) fetch_token<NI>(a.x + (size_t)b * a.H, lane, batch[b]);
   float4 wr[NI];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) wr[i] = *reinterpret_cast<const float4*>(a.wr + (size_t)er * a.H + 256 * i + 4 * lane);
+  for (int i = 0; i < NI; ++i) wr[i] = ld_stream_f4(a.wr + (size_t)er * a.H + 256 * i + 4 * lane);
   for (int t0 = 0; t0 < a.M; t0 += kRouteBatch) {
     if (t0 > 0) {
 #pragma unroll
