@@ -577,7 +577,7 @@ def read_ceiling(ctx, gib=2, runs=5):
     log(f"read ceiling: {gbs:.0f} GB/s ({gib} GiB, 10 KB tiles per wavefront, {blocks} workgroups; runs "
         f"{', '.join(f'{r:.0f}' for r in res)})")
     return {"gbs": round(gbs, 1), "frac_of_peak": round(gbs / PEAK_HBM_GBS, 4), "bytes": n,
-            "kernel": "moe_probe_read (10 KB tiles per wavefront, double-buffered 16-byte loads, every byte once)"}
+            "kernel": "moe_probe_read (10 KB tiles per wavefront, double-buffered 16-byte non-temporal loads, every byte once)"}
 
 
 def summary(r, ceiling):

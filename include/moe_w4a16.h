@@ -342,7 +342,7 @@ const char* moe_status_string(int status);
 
 /* Measurement aid, not part of the layer: reads `bytes` of device memory at
  * `buf` once (each wavefront of `blocks` workgroups of 256 threads takes
- * contiguous 10 KB tiles in turn, 16-byte loads, the next tile requested before
+ * contiguous 10 KB tiles in turn, 16-byte non-temporal loads, the next tile requested before
  * the current one is folded) and writes nothing unless the xor of the data
  * equals a fixed value (then one word per workgroup into sink[blocks], device
  * memory).  The pages find decode bound by weight reads (bpdata.com article,

@@ -148,7 +148,7 @@ __global__ __launch_bounds__(256) void k_lmhead_gemv(const uint8_t* __restrict__
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int c = lane + kWave * i;
-      w[i] = c < nc ? *reinterpret_cast<const uint4*>(base + (size_t)c * 16) : make_uint4(0, 0, 0, 0);
+      w[i] = c < nc ? ld_stream(base + (size_t)c * 16) : make_uint4(0, 0, 0, 0);
     }
   };
   auto compute = [&](const uint4 (&w)[NCH], int p) {

@@ -1,7 +1,8 @@
 // probe.hip — the achievable HBM read rate of this part, measured the way the
-// weight-streaming kernels read: 16-byte loads, whole wavefronts over
-// contiguous 1 KB runs, several kilobytes in flight per wavefront, every byte
-// read once.  The layer's achieved GB/s is
+// weight-streaming kernels read: 16-byte non-temporal loads (data read once
+// passes by the CU's vector cache; on this part they read ~13% faster than
+// plain loads), whole wavefronts over contiguous 1 KB runs, several kilobytes
+// in flight per wavefront, every byte read once.  The layer's achieved GB/s is
 // reported against this ceiling as well as against the nominal peak.
 #include "moe_w4a16.h"
 
@@ -11,6 +12,7 @@
 namespace {
 
 constexpr int kProbeBlock = 256;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 constexpr int kProbeTile = 10;  // 1 KB wavefront loads per tile (10 KB contiguous)
 
 // Each wavefront reads contiguous 10 KB tiles (ten 1 KB loads), the tiles
@@ -31,7 +33,10 @@ __global__ __launch_bounds__(kProbeBlock) void k_read_probe(const uint4* __restr
   uint4 a[kProbeTile], b[kProbeTile];
   auto load = [&](uint4 (&v)[kProbeTile], size_t t) {
 #pragma unroll
-    for (int u = 0; u < kProbeTile; ++u) v[u] = p[t * per_tile + (size_t)u * 64 + lane];
+    for (int u = 0; u < kProbeTile; ++u) {
+      const u32x4_t q = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p + t * per_tile + (size_t)u * 64 + lane));
+      v[u] = make_uint4(q.x, q.y, q.z, q.w);
+    }
   };
   auto fold = [&](const uint4 (&v)[kProbeTile]) {
 #pragma unroll
