@@ -280,7 +280,7 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgItem& it, uint16
       const uint16_t* ss = se + (size_t)((g0 >> a.pshift) * kWave * a.P + (g0 & (a.P - 1)));
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        r.c[nb] = ld_stream(qs + boff[nb]);
+        r.c[nb] = *reinterpret_cast<const uint4*>(qs + boff[nb]);
         r.s[nb] = ss[soff[nb]];
       }
     } else {
@@ -289,7 +289,7 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgItem& it, uint16
 #pragma unroll
         for (int i = 0; i < 4; ++i) {  // 8-input chunk 8st + 2i + h
           const uint8_t* ws = sw + (size_t)(8 * st + 2 * i) * (kWave * 16);
-          r.c[nb][i] = ld_stream(ws + boff[nb]);
+          r.c[nb][i] = *reinterpret_cast<const uint4*>(ws + boff[nb]);
         }
     }
   };
