@@ -216,19 +216,31 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgItem& it, uint16
       aoff[jj] = (uint32_t)sSrc[R] * rowbytes;
     aoff[jj] += seg * 16;
   }
-  // staging registers: one named value per row group (an indexed array here
-  // ends up in scratch memory)
+  // staging registers: two sets (chunks of alternate parity) of one named
+  // value per row group (an indexed array here ends up in scratch memory)
   uint4 st_0, st_1, st_2, st_3, st_4, st_5, st_6, st_7;
-  auto slot = [&](auto J) -> uint4& {
+  uint4 su_0, su_1, su_2, su_3, su_4, su_5, su_6, su_7;
+  auto slot = [&](auto S, auto J) -> uint4& {
     constexpr int j = decltype(J)::value;
-    if constexpr (j == 0) return st_0;
-    else if constexpr (j == 1) return st_1;
-    else if constexpr (j == 2) return st_2;
-    else if constexpr (j == 3) return st_3;
-    else if constexpr (j == 4) return st_4;
-    else if constexpr (j == 5) return st_5;
-    else if constexpr (j == 6) return st_6;
-    else return st_7;
+    if constexpr (decltype(S)::value == 0) {
+      if constexpr (j == 0) return st_0;
+      else if constexpr (j == 1) return st_1;
+      else if constexpr (j == 2) return st_2;
+      else if constexpr (j == 3) return st_3;
+      else if constexpr (j == 4) return st_4;
+      else if constexpr (j == 5) return st_5;
+      else if constexpr (j == 6) return st_6;
+      else return st_7;
+    } else {
+      if constexpr (j == 0) return su_0;
+      else if constexpr (j == 1) return su_1;
+      else if constexpr (j == 2) return su_2;
+      else if constexpr (j == 3) return su_3;
+      else if constexpr (j == 4) return su_4;
+      else if constexpr (j == 5) return su_5;
+      else if constexpr (j == 6) return su_6;
+      else return su_7;
+    }
   };
   auto for_each_jj = [&](auto f) {
     auto one = [&](auto J) {
@@ -240,14 +252,14 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgItem& it, uint16
     one(std::integral_constant<int, 4>{}); one(std::integral_constant<int, 5>{});
     one(std::integral_constant<int, 6>{}); one(std::integral_constant<int, 7>{});
   };
-  auto load_A = [&](int kc0) {
+  auto load_A = [&](auto S, int kc0) {
     const uint8_t* ab = abase8 + 2 * kc0;
-    for_each_jj([&](auto J) { slot(J) = *reinterpret_cast<const uint4*>(ab + aoff[decltype(J)::value]); });
+    for_each_jj([&](auto J) { slot(S, J) = *reinterpret_cast<const uint4*>(ab + aoff[decltype(J)::value]); });
   };
-  auto store_A = [&](int buf) {
+  auto store_A = [&](auto S, int buf) {
     for_each_jj([&](auto J) {
       constexpr int j = decltype(J)::value;
-      *reinterpret_cast<uint4*>(&sA[buf][((tid >> 4) + 16 * j) * kGgStride + seg * 8]) = slot(J);
+      *reinterpret_cast<uint4*>(&sA[buf][((tid >> 4) + 16 * j) * kGgStride + seg * 8]) = slot(S, J);
     });
   };
   // ---- this wavefront's weight tile (tiles past the last read tile 0 and are dropped)
@@ -358,16 +370,21 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgItem& it, uint16
     }
   };
   // ---- main loop: 64-K steps, weights DEPTH - 1 steps ahead in registers,
-  // activations one 128-K chunk ahead in registers, double-buffered in LDS
+  // activations two 128-K chunks ahead in registers, double-buffered in LDS
   const int nsteps = a.K / 64;  // a multiple of 4
   const int nch = nsteps / 2;
   Raw ring[C::DEPTH];
 #pragma unroll
   for (int d = 0; d < C::DEPTH - 1; ++d) load_B(d, ring[d]);
-  load_A(0);
-  store_A(0);
+  // chunks 1, 3, 5, ... stage in the first register set, 2, 4, ... in the
+  // second, so each chunk's rows are requested two chunks before they go to LDS
+  constexpr std::integral_constant<int, 0> odd{};
+  constexpr std::integral_constant<int, 1> even{};
+  load_A(odd, 0);
+  store_A(odd, 0);
   lds_sync();
-  load_A(kGgKc);
+  load_A(odd, kGgKc);
+  load_A(even, min(2, nch - 1) * kGgKc);
   for (int st0 = 0; st0 < nsteps; st0 += 4) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -375,12 +392,19 @@ __device__ __forceinline__ void gg_run(const GgArgs& a, const GgItem& it, uint16
       load_B(min(st + C::DEPTH - 1, nsteps - 1), ring[(u + C::DEPTH - 1) % C::DEPTH]);
       compute(ring[u % C::DEPTH], (u >> 1) & 1, 64 * (u & 1));
       if (u & 1) {
-        // end of chunk ch = st / 2: chunk ch + 1 into the other buffer (its last
-        // readers, chunk ch - 1, all passed the previous barrier)
+        // end of chunk ch = st / 2 (even at u = 1, odd at u = 3): chunk ch + 1
+        // into the other buffer (its last readers, chunk ch - 1, all passed
+        // the previous barrier), then chunk ch + 3 into the freed registers
         const int ch = st >> 1;
-        store_A(((u >> 1) + 1) & 1);
-        lds_sync();
-        load_A(min(ch + 2, nch - 1) * kGgKc);
+        if (u == 1) {
+          store_A(odd, 1);
+          lds_sync();
+          load_A(odd, min(ch + 3, nch - 1) * kGgKc);
+        } else {
+          store_A(even, 0);
+          lds_sync();
+          load_A(even, min(ch + 3, nch - 1) * kGgKc);
+        }
       }
     }
   }
