@@ -46,10 +46,10 @@ def _layer(dl, x_dev, flags=None, x_norm=None):
     return ids, w, out
 
 
-def _check_layer(dl, oracle, x_bits, what):
+def _check_layer(dl, oracle, x_bits, what, flags=None):
     import torch
     x_dev = to_dev_bf16(x_bits)
-    ids, w, out = _layer(dl, x_dev)
+    ids, w, out = _layer(dl, x_dev, flags=flags)
     torch.cuda.synchronize()
     assert dl.device_error() == 0, what
     ids_g, w_g = ids.cpu().numpy(), w.cpu().numpy()
@@ -69,6 +69,24 @@ def test_layer_ling_matches_oracle(ling, oracle_mod, M):
     x = synth.make_tokens(synth.LING, 500 + M, steps * M)
     worst = max(_check_layer(ling, oracle_mod, x[s * M:(s + 1) * M], f"layer ling M={M} step {s}") for s in range(steps))
     _say(f"layer ling M={M}: worst ratio {worst:.3e}")
+
+
+@pytest.mark.parametrize("M", [2, 3, 4])
+def test_layer_default_dispatch_matches_oracle(ling, oracle_mod, M):
+    """moe_layer_w4a16 with no flags, as a speculative-verify step calls it:
+    the library picks the kernels for M tokens itself.  Eight steps of
+    seeded Ling tokens, each against the oracle, and the routing equal to
+    moe_route's bit for bit."""
+    import torch
+    x = synth.make_tokens(synth.LING, 700 + M, 8 * M)
+    for s in range(8):
+        xs = x[s * M:(s + 1) * M]
+        _check_layer(ling, oracle_mod, xs, f"default dispatch M={M} step {s}", flags=0)
+        x_dev = to_dev_bf16(xs)
+        ids, w, _ = _layer(ling, x_dev, flags=0)
+        r_ids, r_w = ling.route(x_dev)
+        torch.cuda.synchronize()
+        assert torch.equal(ids, r_ids) and torch.equal(w, r_w)
 
 
 def test_layer_after_larger_calls(ling, oracle_mod):
