@@ -475,7 +475,8 @@ __device__ __forceinline__ void gg_item(const GgArgs& a, int b, uint16_t (*sA)[k
     le = exp_bound(__uint_as_float(mt[2]));
     it.ey = 1 - it.p - exp_above(__uint_as_float(mt[3]));
   }
-  // ---- row tables: A source row and the exponents of each row
+  // ---- row tables: A source row of each row, and for gate_up the row
+  // exponents its epilogue needs (the down epilogue needs only it.ey)
   if (tid < C::ROWS) {
     const int rr = tid < it.nrow ? tid : 0;  // padding rows repeat row 0; their results are dropped
     if constexpr (KIND == GG_RGU) {
@@ -483,10 +484,6 @@ __device__ __forceinline__ void gg_item(const GgArgs& a, int b, uint16_t (*sA)[k
       sSrc[tid] = tok;
       sExp[tid] = a.rexp[2 * tok];
       sSig[tid] = a.rexp[2 * tok + 1] + le - 13;
-    } else if constexpr (KIND == GG_RDN) {
-      const int tok = a.perm[it.base + rr] / a.k;
-      sSrc[tid] = it.base + rr;
-      sExp[tid] = a.rexp[2 * tok + 1] + le - 13;
     } else {
       sSrc[tid] = it.base + rr;
     }
