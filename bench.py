@@ -481,7 +481,8 @@ def measure_fmt(ctx, wl, K, W):
             "us_per_token": ms_per_step * 1e3, "bytes_per_step": float(nbytes), "resident_layer_copies": FMT_COPIES,
             "us_per_token_two_calls": round(ms_calls * 1e3, 3),
             "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": measured_traffic(WORKLOAD_NAMES[wl]) if one else None,
                          "bytes_per_launch": nbytes, "us_per_launch": round(ms_per_step * 1e3, 3)}}
 
 
